@@ -1,0 +1,169 @@
+/*
+ * onela.h - C ABI of the OneLA large-beam Gated DeltaNet decode step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (OneLA abstract, readsearch.ai page; OneLA review,
+ * evolve.pub, "Summary", "Key claims", "Scope & Claims", paper Eq. 2-4):
+ * every request holds ONE prompt-derived state S0 per head (d_v x d_k) that
+ * all W beams share. At decode step t each beam b of a request, whose history
+ * is the list of transition records (alpha_j, delta_j, k_j) of its ancestors,
+ * advances the GDN recurrence
+ *
+ *     delta_t = beta_t * (v_t - alpha_t * S_{t-1} k_t)
+ *     S_t     = alpha_t * S_{t-1} + delta_t k_t^T
+ *     o_t     = S_t q_t
+ *
+ * without ever forming its own S: S_{t-1} x (x = k_t, q_t) is S0 x plus a
+ * replay of the ancestral records, y <- alpha_j y + (k_j . x) delta_j. The step
+ * then appends the record (alpha_t, delta_t, k_t) for the beam and returns o_t.
+ * Records are append-only; an ancestry index (one per request, shared by all
+ * heads) lists the record ids of each beam's history. When beams fork only
+ * record ids are copied, never records.
+ *
+ * Conventions used by this library (the pages do not fix them):
+ *   - steps are t = 1..max_steps per episode; at t = 1 all beams start from
+ *     S0 and parent_idx is ignored;
+ *   - the record of beam b written at step t has id rid = (t-1)*W + b;
+ *   - ancestry row of beam b at step t = record ids of its t-1 ancestors,
+ *     oldest first;
+ *   - no query scaling and no normalisation inside: the caller folds those
+ *     into q and k;
+ *   - alpha, beta are one float per (beam, head); S0, delta, o are float32;
+ *     q, k, v are bf16 (passed as uint16_t bit patterns).
+ *
+ * Memory and execution:
+ *   - every pointer marked "device" is HIP device memory owned by the caller,
+ *     which must keep it alive until the work enqueued on the context's
+ *     stream has finished;
+ *   - the library owns its state (S0 planes, record store, ancestry index,
+ *     error words) and allocates all of it in onela_create; onela_step
+ *     allocates nothing;
+ *   - every call that launches work is asynchronous on the stream given to
+ *     onela_create; getters synchronise that stream;
+ *   - one host thread at a time per context.
+ *
+ * Errors: every function returns ONELA_OK (0) or a negative status. Misuse
+ * that the host can see (NULL pointers, bad ids, wrong state, capacity) is
+ * rejected before anything is enqueued and leaves the context unchanged. A
+ * parent index outside [0, W) is found on the device: the affected request's
+ * outputs for that step are undefined, the request is poisoned, and the next
+ * onela_sync or getter for it returns ONELA_E_PARENT_RANGE; onela_reset or
+ * onela_init_request clears the poison.
+ */
+#ifndef ONELA_H
+#define ONELA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t onela_status;
+
+#define ONELA_OK               0
+#define ONELA_E_INVALID_ARG   (-1)  /* NULL pointer, id out of range, duplicate id */
+#define ONELA_E_BAD_STATE     (-2)  /* request not initialised, or poisoned */
+#define ONELA_E_CAPACITY      (-3)  /* request already did max_steps steps */
+#define ONELA_E_PARENT_RANGE  (-4)  /* a parent index was outside [0, W) */
+#define ONELA_E_HIP           (-5)  /* a HIP call failed; see onela_last_error */
+#define ONELA_E_OOM           (-6)  /* device allocation failed in onela_create */
+#define ONELA_E_UNSUPPORTED   (-7)  /* head dims or step count this build has no kernel for */
+
+/* Fixed shape of one context (one GDN layer). Supported: d_k == d_v in
+ * {32, 64, 128}; 1 <= beam_width; 1 <= max_steps <= ONELA_MAX_STEPS. */
+#define ONELA_MAX_STEPS 64
+
+typedef struct onela_config {
+    int32_t max_requests;  /* request slots, ids 0..max_requests-1 */
+    int32_t num_heads;     /* H; heads are independent (equal q/k/v head counts) */
+    int32_t d_k;
+    int32_t d_v;
+    int32_t beam_width;    /* W */
+    int32_t max_steps;     /* decode steps per episode (record store depth) */
+} onela_config;
+
+typedef struct onela_ctx onela_ctx;
+
+/* Create a context on the current HIP device. hip_stream is a hipStream_t
+ * (NULL = the null stream). Allocates S0 planes (4*H*d_v*d_k bytes per
+ * request), the record store ((4 + 4*d_v + 2*d_k) bytes per record,
+ * max_requests*H*max_steps*W records) and the ancestry index
+ * (2*max_requests*W*max_steps int32). On failure *out is NULL. */
+onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out);
+
+/* Synchronise the stream and free everything the context owns. NULL is OK. */
+onela_status onela_destroy(onela_ctx* ctx);
+
+/* Load the shared prompt-derived state of request `req` and rewind it to
+ * step 0 (OneLA abstract: one shared prompt-derived state per request).
+ * S0: device float32 [H][d_v][d_k], row-major (rows index d_v). The library
+ * keeps its own copy (split into two bf16 planes whose sum carries S0 to
+ * about 2^-17 relative), so S0 may be freed once the stream has passed this
+ * call. */
+onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0);
+
+/* One decode step of one GDN layer for n_req requests (OneLA review,
+ * "Key claims" and "Scope & Claims", paper Eq. 2-4: records (alpha, delta, k)
+ * appended per step, projection replay over the ancestry).
+ *   reqs       host int32 [n_req], distinct initialised request ids; each
+ *              request advances its own step counter t (requests may be at
+ *              different depths).
+ *   q, k       device bf16 [n_req*W][H][d_k]   (request i owns rows i*W..)
+ *   v          device bf16 [n_req*W][H][d_v]
+ *   alpha,beta device float32 [n_req*W][H]
+ *   parent_idx device int32 [n_req][W]: beam b of request i continues beam
+ *              parent_idx[i][b] of the previous step. Read only for requests
+ *              at t >= 2; may be NULL if every request is at t == 1.
+ *   o          device float32 [n_req*W][H][d_v], written (o_t = S_t q_t)
+ *   delta_out  optional device float32 [n_req*W][H][d_v]; receives delta_t
+ *              (the same values appended to the record store), or NULL.
+ * Nothing is allocated. Returns after enqueueing. */
+onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
+                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* alpha, const float* beta,
+                        const int32_t* parent_idx, float* o, float* delta_out);
+
+/* Rewind request `req` to step 0, keeping its S0 (the records of the old
+ * episode become dead and are overwritten by the next one). Host-only, O(1),
+ * except that the request's device error word is cleared on the stream. */
+onela_status onela_reset(onela_ctx* ctx, int32_t req);
+
+/* Wait for the stream. Returns ONELA_E_PARENT_RANGE if any request is
+ * poisoned by a bad parent index, ONELA_E_HIP on a HIP failure. */
+onela_status onela_sync(onela_ctx* ctx);
+
+/* Beams handled by one workgroup (0 = automatic). Must be 0 or a multiple of
+ * 64. Results do not depend on it; only the launch shape does. */
+onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
+
+/* ---- inspection (synchronous; for tests and accounting) ---------------- */
+
+/* Steps done by `req` in the current episode (0 after init or reset). */
+onela_status onela_get_step(onela_ctx* ctx, int32_t req, int32_t* t_done);
+
+/* Ancestry rows the last step of `req` used: host int32 [W][max_steps];
+ * row b holds t_done-1 record ids (oldest first) and -1 after them. */
+onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out);
+
+/* Records 0..n_rec-1 of (req, head), n_rec <= t_done*W. Host outputs, each
+ * may be NULL: alpha float32 [n_rec], delta float32 [n_rec][d_v],
+ * key bf16 bits [n_rec][d_k]. */
+onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_t n_rec,
+                               float* alpha, float* delta, uint16_t* key);
+
+/* Device bytes the context owns: S0 planes, record store, ancestry index. */
+onela_status onela_get_memory(const onela_ctx* ctx, uint64_t* s0_bytes,
+                              uint64_t* record_bytes, uint64_t* index_bytes);
+
+/* Static text for a status code. */
+const char* onela_status_string(onela_status s);
+
+/* Text of the last HIP error seen by this context ("" if none). */
+const char* onela_last_error(const onela_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONELA_H */

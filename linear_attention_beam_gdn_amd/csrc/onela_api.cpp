@@ -1,0 +1,304 @@
+// Host runtime and C ABI of the OneLA GDN decode step (declared in onela.h).
+//
+// A context is one GDN layer: fixed-capacity, library-owned device buffers
+// for the shared states, the append-only record store and the ancestry index,
+// plus host-side step counters per request. onela_step validates on the host,
+// then enqueues one step launch per group of up to kMaxReqPerLaunch requests.
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/onela.h"
+#include "onela_internal.h"
+
+struct onela_ctx {
+    onela_config cfg;
+    hipStream_t stream = nullptr;
+    int device = 0;
+    uint16_t* s0_planes = nullptr;
+    float* rec_alpha = nullptr;
+    float* rec_delta = nullptr;
+    uint16_t* rec_k = nullptr;
+    int32_t* anc = nullptr;
+    int32_t* err = nullptr;
+    std::vector<int32_t> steps;      // steps done per request; -1 = never initialised
+    std::vector<char> poisoned;      // a bad parent index was reported
+    std::vector<int32_t> err_host;
+    int32_t beams_per_block = 0;     // 0 = automatic
+    std::string last_error;
+    uint64_t s0_bytes = 0, rec_bytes = 0, idx_bytes = 0;
+};
+
+namespace {
+
+onela_status hip_fail(onela_ctx* ctx, hipError_t e, const char* what) {
+    if (ctx) ctx->last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return ONELA_E_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_req(const onela_ctx* ctx, int32_t req) {
+    return req >= 0 && req < ctx->cfg.max_requests;
+}
+
+// Copy the device error words to the host and poison every flagged request.
+onela_status drain(onela_ctx* ctx) {
+    hipError_t e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+    e = hipMemcpy(ctx->err_host.data(), ctx->err, sizeof(int32_t) * ctx->cfg.max_requests,
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(err)");
+    for (int r = 0; r < ctx->cfg.max_requests; ++r)
+        if (ctx->err_host[r]) ctx->poisoned[r] = 1;
+    return ONELA_OK;
+}
+
+int auto_beams_per_block(const onela_ctx* ctx, int n_pairs) {
+    // Enough workgroups to give each of the 256 CUs several, while keeping
+    // as many beams as possible per workgroup (S0 stays in registers across
+    // them).
+    const int W = ctx->cfg.beam_width;
+    const int chunks = (W + onela::kChunk - 1) / onela::kChunk;
+    int splits = std::max(1, std::min(chunks, (1024 + n_pairs - 1) / n_pairs));
+    const int per = (chunks + splits - 1) / splits;
+    return per * onela::kChunk;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* onela_status_string(onela_status s) {
+    switch (s) {
+        case ONELA_OK: return "ok";
+        case ONELA_E_INVALID_ARG: return "invalid argument";
+        case ONELA_E_BAD_STATE: return "request not initialised or poisoned";
+        case ONELA_E_CAPACITY: return "request has no step left (max_steps reached)";
+        case ONELA_E_PARENT_RANGE: return "parent index outside [0, W)";
+        case ONELA_E_HIP: return "HIP error";
+        case ONELA_E_OOM: return "device allocation failed";
+        case ONELA_E_UNSUPPORTED: return "unsupported shape";
+        default: return "unknown status";
+    }
+}
+
+const char* onela_last_error(const onela_ctx* ctx) { return ctx ? ctx->last_error.c_str() : ""; }
+
+onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out) {
+    if (!out) return ONELA_E_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg || cfg->max_requests < 1 || cfg->num_heads < 1 || cfg->beam_width < 1 || cfg->max_steps < 1 ||
+        cfg->d_k < 1 || cfg->d_v < 1)
+        return ONELA_E_INVALID_ARG;
+    if (!onela::step_supported(cfg->d_k, cfg->d_v) || cfg->max_steps > ONELA_MAX_STEPS)
+        return ONELA_E_UNSUPPORTED;
+
+    onela_ctx* ctx = new onela_ctx();
+    ctx->cfg = *cfg;
+    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    (void)hipGetDevice(&ctx->device);
+    const uint64_t R = cfg->max_requests, H = cfg->num_heads, W = cfg->beam_width, T = cfg->max_steps;
+    const uint64_t dk = cfg->d_k, dv = cfg->d_v;
+    const uint64_t nrec = R * H * T * W;
+    ctx->s0_bytes = R * H * 2 * dv * dk * 2;
+    ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
+    ctx->idx_bytes = 2 * R * W * T * 4 + R * 4;
+
+    bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
+              hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
+              hipMalloc(&ctx->rec_delta, nrec * 4 * dv) == hipSuccess &&
+              hipMalloc(&ctx->rec_k, nrec * 2 * dk) == hipSuccess &&
+              hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess &&
+              hipMalloc(&ctx->err, R * 4) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        onela_destroy(ctx);
+        return ONELA_E_OOM;
+    }
+    if (hipMemsetAsync(ctx->err, 0, R * 4, ctx->stream) != hipSuccess ||
+        hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess) {
+        onela_destroy(ctx);
+        return ONELA_E_HIP;
+    }
+    ctx->steps.assign(R, -1);
+    ctx->poisoned.assign(R, 0);
+    ctx->err_host.assign(R, 0);
+    *out = ctx;
+    return ONELA_OK;
+}
+
+onela_status onela_destroy(onela_ctx* ctx) {
+    if (!ctx) return ONELA_OK;
+    (void)hipStreamSynchronize(ctx->stream);
+    (void)hipFree(ctx->s0_planes);
+    (void)hipFree(ctx->rec_alpha);
+    (void)hipFree(ctx->rec_delta);
+    (void)hipFree(ctx->rec_k);
+    (void)hipFree(ctx->anc);
+    (void)hipFree(ctx->err);
+    delete ctx;
+    return ONELA_OK;
+}
+
+onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0) {
+    if (!ctx || !S0 || !valid_req(ctx, req) || !aligned(S0, 16)) return ONELA_E_INVALID_ARG;
+    const auto& c = ctx->cfg;
+    uint16_t* planes = ctx->s0_planes + (size_t)req * c.num_heads * 2 * c.d_v * c.d_k;
+    hipError_t e = onela::launch_init_s0(c.d_k, c.d_v, S0, planes, c.num_heads, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "init_s0 launch");
+    e = hipMemsetAsync(ctx->err + req, 0, 4, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemsetAsync(err)");
+    ctx->steps[req] = 0;
+    ctx->poisoned[req] = 0;
+    ctx->err_host[req] = 0;
+    return ONELA_OK;
+}
+
+onela_status onela_reset(onela_ctx* ctx, int32_t req) {
+    if (!ctx || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
+    if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
+    hipError_t e = hipMemsetAsync(ctx->err + req, 0, 4, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemsetAsync(err)");
+    ctx->steps[req] = 0;
+    ctx->poisoned[req] = 0;
+    ctx->err_host[req] = 0;
+    return ONELA_OK;
+}
+
+onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams) {
+    if (!ctx || beams < 0 || beams % onela::kChunk != 0) return ONELA_E_INVALID_ARG;
+    ctx->beams_per_block = beams;
+    return ONELA_OK;
+}
+
+onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+                        const int32_t* parent_idx, float* o, float* delta_out) {
+    if (!ctx || n_req < 1 || n_req > ctx->cfg.max_requests || !reqs || !q || !k || !v || !alpha || !beta || !o)
+        return ONELA_E_INVALID_ARG;
+    // vector loads and stores: 16 B for q, k, o, delta_out; 8 B for v; 4 B for the rest
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 8) || !aligned(o, 16) || !aligned(delta_out, 16) ||
+        !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(parent_idx, 4))
+        return ONELA_E_INVALID_ARG;
+    const auto& c = ctx->cfg;
+    std::vector<char> seen(c.max_requests, 0);
+    bool need_parents = false;
+    for (int i = 0; i < n_req; ++i) {
+        const int r = reqs[i];
+        if (!valid_req(ctx, r) || seen[r]) return ONELA_E_INVALID_ARG;
+        seen[r] = 1;
+        if (ctx->steps[r] < 0 || ctx->poisoned[r]) return ONELA_E_BAD_STATE;
+        if (ctx->steps[r] >= c.max_steps) return ONELA_E_CAPACITY;
+        if (ctx->steps[r] >= 1) need_parents = true;
+    }
+    if (need_parents && !parent_idx) return ONELA_E_INVALID_ARG;
+
+    onela::StepParams p{};
+    p.s0_planes = ctx->s0_planes;
+    p.rec_alpha = ctx->rec_alpha;
+    p.rec_delta = ctx->rec_delta;
+    p.rec_k = ctx->rec_k;
+    p.anc = ctx->anc;
+    p.err = ctx->err;
+    p.H = c.num_heads;
+    p.W = c.beam_width;
+    p.T_max = c.max_steps;
+    p.max_requests = c.max_requests;
+    const size_t W = c.beam_width, H = c.num_heads;
+    for (int i0 = 0; i0 < n_req; i0 += onela::kMaxReqPerLaunch) {
+        const int n = std::min(onela::kMaxReqPerLaunch, n_req - i0);
+        const size_t rows = (size_t)i0 * W;
+        p.q = q + rows * H * c.d_k;
+        p.k = k + rows * H * c.d_k;
+        p.v = v + rows * H * c.d_v;
+        p.alpha = alpha + rows * H;
+        p.beta = beta + rows * H;
+        p.parent = parent_idx ? parent_idx + rows : nullptr;
+        p.o = o + rows * H * c.d_v;
+        p.delta_out = delta_out ? delta_out + rows * H * c.d_v : nullptr;
+        p.n_req = n;
+        p.beams_per_block = ctx->beams_per_block ? ctx->beams_per_block : auto_beams_per_block(ctx, n * c.num_heads);
+        p.n_splits = (c.beam_width + p.beams_per_block - 1) / p.beams_per_block;
+        for (int i = 0; i < n; ++i) {
+            p.slot[i] = reqs[i0 + i];
+            p.t[i] = ctx->steps[reqs[i0 + i]] + 1;
+        }
+        hipError_t e = onela::launch_step(c.d_k, c.d_v, p, ctx->stream);
+        if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
+        for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;
+    }
+    return ONELA_OK;
+}
+
+onela_status onela_sync(onela_ctx* ctx) {
+    if (!ctx) return ONELA_E_INVALID_ARG;
+    onela_status s = drain(ctx);
+    if (s != ONELA_OK) return s;
+    for (int r = 0; r < ctx->cfg.max_requests; ++r)
+        if (ctx->poisoned[r]) return ONELA_E_PARENT_RANGE;
+    return ONELA_OK;
+}
+
+onela_status onela_get_step(onela_ctx* ctx, int32_t req, int32_t* t_done) {
+    if (!ctx || !t_done || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
+    if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
+    onela_status s = drain(ctx);
+    if (s != ONELA_OK) return s;
+    *t_done = ctx->steps[req];
+    return ctx->poisoned[req] ? ONELA_E_PARENT_RANGE : ONELA_OK;
+}
+
+onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out) {
+    if (!ctx || !host_out || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
+    if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
+    onela_status s = drain(ctx);
+    if (s != ONELA_OK) return s;
+    if (ctx->poisoned[req]) return ONELA_E_PARENT_RANGE;
+    const auto& c = ctx->cfg;
+    const size_t n = (size_t)c.beam_width * c.max_steps;
+    const int t = ctx->steps[req];
+    std::fill(host_out, host_out + n, -1);
+    if (t >= 2) {
+        std::vector<int32_t> buf(n);
+        const int32_t* src = ctx->anc + ((size_t)(t & 1) * c.max_requests + req) * n;
+        hipError_t e = hipMemcpy(buf.data(), src, n * 4, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(anc)");
+        for (int b = 0; b < c.beam_width; ++b)
+            for (int j = 0; j < t - 1; ++j) host_out[(size_t)b * c.max_steps + j] = buf[(size_t)b * c.max_steps + j];
+    }
+    return ONELA_OK;
+}
+
+onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_t n_rec, float* alpha,
+                               float* delta, uint16_t* key) {
+    if (!ctx || !valid_req(ctx, req) || head < 0 || head >= ctx->cfg.num_heads || n_rec < 0)
+        return ONELA_E_INVALID_ARG;
+    if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
+    const auto& c = ctx->cfg;
+    if ((int64_t)n_rec > (int64_t)ctx->steps[req] * c.beam_width) return ONELA_E_INVALID_ARG;
+    onela_status s = drain(ctx);
+    if (s != ONELA_OK) return s;
+    if (ctx->poisoned[req]) return ONELA_E_PARENT_RANGE;
+    const size_t rec0 = ((size_t)req * c.num_heads + head) * (size_t)c.max_steps * c.beam_width;
+    hipError_t e = hipSuccess;
+    if (alpha && n_rec) e = hipMemcpy(alpha, ctx->rec_alpha + rec0, (size_t)n_rec * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && delta && n_rec)
+        e = hipMemcpy(delta, ctx->rec_delta + rec0 * c.d_v, (size_t)n_rec * 4 * c.d_v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && key && n_rec)
+        e = hipMemcpy(key, ctx->rec_k + rec0 * c.d_k, (size_t)n_rec * 2 * c.d_k, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(records)");
+    return ONELA_OK;
+}
+
+onela_status onela_get_memory(const onela_ctx* ctx, uint64_t* s0_bytes, uint64_t* record_bytes,
+                              uint64_t* index_bytes) {
+    if (!ctx) return ONELA_E_INVALID_ARG;
+    if (s0_bytes) *s0_bytes = ctx->s0_bytes;
+    if (record_bytes) *record_bytes = ctx->rec_bytes;
+    if (index_bytes) *index_bytes = ctx->idx_bytes;
+    return ONELA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI host runtime and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace onela {
+
+// Requests one step launch carries in its kernel arguments; onela_step splits
+// larger calls into several launches.
+constexpr int kMaxReqPerLaunch = 64;
+// Beams one workgroup stages at a time (one chunk of the beam loop).
+constexpr int kChunk = 64;
+
+struct StepParams {
+    // caller inputs / outputs
+    const uint16_t* q;       // bf16 [n_req*W][H][DK]
+    const uint16_t* k;       // bf16 [n_req*W][H][DK]
+    const uint16_t* v;       // bf16 [n_req*W][H][DV]
+    const float* alpha;      // [n_req*W][H]
+    const float* beta;       // [n_req*W][H]
+    const int32_t* parent;   // [n_req][W] (unused for requests at t == 1)
+    float* o;                // [n_req*W][H][DV]
+    float* delta_out;        // optional, like o
+    // library state
+    const uint16_t* s0_planes;  // [max_requests][H][2][DV*DK] in MFMA fragment order
+    float* rec_alpha;           // [max_requests][H][T_max*W]
+    float* rec_delta;           // [max_requests][H][T_max*W][DV]
+    uint16_t* rec_k;            // [max_requests][H][T_max*W][DK]
+    int32_t* anc;               // [2][max_requests][W][T_max] (ping-pong by step parity)
+    int32_t* err;               // [max_requests]
+    int32_t H, W, T_max, max_requests;
+    int32_t beams_per_block;    // multiple of kChunk, or >= W
+    int32_t n_splits;           // ceil(W / beams_per_block)
+    int32_t n_req;
+    int32_t slot[kMaxReqPerLaunch];  // request id of call-local request i
+    int32_t t[kMaxReqPerLaunch];     // step this launch performs for it (1-based)
+};
+
+// Returns hipErrorInvalidValue for unsupported (DK, DV).
+hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
+hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
+bool step_supported(int dk, int dv);
+size_t step_lds_bytes(int dk, int T_max);
+
+}  // namespace onela

@@ -1,0 +1,122 @@
+"""Parity of the HIP decode step with the float64 oracle (through the C ABI).
+
+Tolerance: max-abs 1e-3 on o and delta at every step (fp32 state and
+accumulation, bf16 inputs); record alpha and key bits, record ids and the
+ancestry index must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gpu_harness as gh
+    from workload import shape_of
+
+
+def _check_pairs(shape, ep, S0, outs, pairs, tol=None):
+    tol = gh.TOL if tol is None else tol
+    W, T = shape.W, shape.T
+    worst = (0.0, 0.0)
+    for (i, h) in pairs:
+        ref = gh.oracle_pair(shape, ep, S0, i, h)
+        eo, ed = gh.max_err(outs, ref, i, h, W)
+        worst = (max(worst[0], eo), max(worst[1], ed))
+        assert eo <= tol and ed <= tol, f"pair {(i, h)}: max err o={eo:.3g} delta={ed:.3g}"
+        for t in range(T):
+            anc = outs["anc"][t][i]
+            np.testing.assert_array_equal(anc[:, :t], ref["anc"][t])
+            assert np.all(anc[:, t:] == -1)
+        a, d, kbits = outs["layer"].get_records(i, h, T * W)
+        sl = slice(i * W, (i + 1) * W)
+        np.testing.assert_array_equal(a.reshape(T, W), ep["alpha"][:, sl, h])
+        np.testing.assert_array_equal(kbits.reshape(T, W, -1), ep["k"][:, sl, h, :])
+        assert np.abs(d - ref["rec_delta"]).max() <= tol
+    print(f"{shape.name}: worst max-abs err o={worst[0]:.3e} delta={worst[1]:.3e} over {len(pairs)} pairs")
+    return worst
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_parity_small_configs(cfg):
+    shape = shape_of(cfg)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] cfg={cfg} {shape.name}", flush=True)
+    outs = gh.run_episode(shape, ep, S0)
+    pairs = [(i, h) for i in range(shape.R) for h in range(shape.H)]
+    _check_pairs(shape, ep, S0, outs, pairs)
+    outs["layer"].close()
+
+
+def test_parity_r32_full_size_sampled():
+    """All 32 requests x 16 heads at W=256, T=5 in the bench's launch shape; sampled pairs vs the oracle."""
+    shape = shape_of(3)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] {shape.name}", flush=True)
+    outs = gh.run_episode(shape, ep, S0, keep_delta=True)
+    rng = np.random.default_rng(3)
+    pairs = [(0, 0), (31, 15)] + [(int(rng.integers(32)), int(rng.integers(16))) for _ in range(4)]
+    _check_pairs(shape, ep, S0, outs, pairs)
+    for t in range(shape.T):
+        assert np.isfinite(outs["o"][t]).all() and np.isfinite(outs["delta"][t]).all()
+    outs["layer"].close()
+
+
+@pytest.mark.parametrize("W,T,H,d", [(1, 3, 2, 32), (65, 4, 3, 64), (130, 5, 2, 128), (200, 2, 1, 128)])
+def test_parity_ragged_beams(W, T, H, d):
+    """Beam counts that leave partial chunks (and W = 1, a plain GDN chain)."""
+    shape = shape_of(0, name=f"ragged_w{W}", H=H, dk=d, dv=d, W=W, T=T, R=2)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] ragged W={W} T={T} H={H} d={d}", flush=True)
+    outs = gh.run_episode(shape, ep, S0)
+    pairs = [(i, h) for i in range(2) for h in range(H)]
+    _check_pairs(shape, ep, S0, outs, pairs)
+    outs["layer"].close()
+
+
+def test_tile_size_invariance_and_determinism():
+    """Outputs are bit-identical across launch shapes and across runs."""
+    shape = shape_of(1, R=2, T=4)
+    ep, S0 = gh.episode(shape)
+    runs = [gh.run_episode(shape, ep, S0, beams_per_block=bpb) for bpb in (0, 64, 128, 256, 0)]
+    for other in runs[1:]:
+        for t in range(shape.T):
+            assert np.array_equal(runs[0]["o"][t], other["o"][t])
+            assert np.array_equal(runs[0]["delta"][t], other["delta"][t])
+    for r in runs:
+        r["layer"].close()
+
+
+def test_requests_at_different_depths():
+    """Requests that join later run at their own step index in the same launch."""
+    shape = shape_of(1, name="mixed_depth", R=3, H=4, T=4)
+    ep, S0 = gh.episode(shape)
+    W, H = shape.W, shape.H
+    lay = gh.Onela(max_requests=5, num_heads=H, d_k=128, d_v=128, beam_width=W, max_steps=shape.T)
+    slots = [4, 0, 2]                                  # library ids of workload requests 0, 1, 2
+    for i, s in enumerate(slots):
+        lay.init_request(s, gh.to_dev(S0[i]))
+    start = [0, 1, 2]                                  # request i joins at call number start[i]
+    o_hist = {i: [] for i in range(3)}
+    for call in range(shape.T + 2):
+        active = [i for i in range(3) if start[i] <= call < start[i] + shape.T]
+        if not active:
+            continue
+        steps = [call - start[i] for i in active]
+        cat = lambda key, t_of: np.concatenate(
+            [ep[key][t_of[j]][i * W:(i + 1) * W] for j, i in enumerate(active)], axis=0)
+        q, k, v = (gh.to_dev(cat(key, steps)) for key in ("q", "k", "v"))
+        a, b = gh.to_dev(cat("alpha", steps)), gh.to_dev(cat("beta", steps))
+        par = gh.to_dev(np.stack([np.maximum(ep["parents"][steps[j]][i], 0) for j, i in enumerate(active)]).astype(np.int32))
+        o = torch.empty((len(active) * W, H, 128), dtype=torch.float32, device=gh.dev())
+        lay.step([slots[i] for i in active], q, k, v, a, b, par, o)
+        lay.sync()
+        on = o.cpu().numpy()
+        for j, i in enumerate(active):
+            o_hist[i].append(on[j * W:(j + 1) * W])
+    for i in range(3):
+        for h in range(H):
+            ref = gh.oracle_pair(shape, ep, S0, i, h)
+            for t in range(shape.T):
+                assert np.abs(o_hist[i][t][:, h] - ref["o"][t]).max() <= gh.TOL
+    lay.close()
