@@ -1,0 +1,288 @@
+"""Throughput of the OneLA GDN beam decode step on one MI355X.
+
+Workload: 32 concurrent requests x 16 heads, d_k = d_v = 128, beam width 256,
+5 decode steps per episode, S0 ~ N(0, 0.05^2) per head, parents chosen per
+request as the top W of 4W beam-search-like candidates. One bench step is one
+episode: every request is rewound (host-only) and advanced through all 5
+decode steps of one GDN layer, one library launch per decode step. All inputs
+of the 5 steps are resident in HBM before timing starts.
+
+Prints one JSON line: beam-steps/s (value), microseconds per decode step, the
+per-depth breakdown, the HBM roofline fraction of the step kernel (algorithmic
+bytes per launch over its average duration from HIP events recorded around
+every launch in the timed region) and the float64 oracle timed on a bounded
+sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workload import bf16_bits_to_f32, make_episode, shape_of  # noqa: E402
+
+METRIC = "GDN beam-steps/sec + µs/decode-step at W=256,d_k=d_v=128; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+KERNEL_NAME = "step_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_r32_h16_w256_t5_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_beam_gdn_amd", "csrc", "onela_kernels.hip")
+
+
+# ------------------------------------------------------------- accounting
+def unique_ancestors(parents_req: np.ndarray, t: int) -> int:
+    """Distinct records the W beams of one request read at step t (1-based)."""
+    if t < 2:
+        return 0
+    total = 0
+    reach = np.unique(parents_req[t - 1])            # beams of step t-1 with a child at step t
+    for s in range(t - 1, 0, -1):
+        total += len(reach)
+        if s > 1:
+            reach = np.unique(parents_req[s - 1][reach])
+    return total
+
+
+def step_bytes(shape, parents, t: int) -> dict:
+    """Algorithmic HBM bytes of one decode step at depth t over all requests and heads."""
+    R, H, W, dk, dv = shape.R, shape.H, shape.W, shape.dk, shape.dv
+    rec = 4 + 4 * dv + 2 * dk
+    uniq = sum(unique_ancestors(parents[:, r, :], t) for r in range(R))
+    b = {
+        "s0": R * H * 4 * dv * dk,                      # hi + lo bf16 planes = fp32 bytes
+        "inputs": R * W * H * (2 * dk + 2 * dk + 2 * dv + 8),
+        "records_read": uniq * H * rec,
+        "records_append": R * W * H * rec,
+        "o": R * W * H * 4 * dv,
+        "ancestry": (R * W * 4 * (1 + 2 * (t - 1) - 1)) if t >= 2 else 0,
+    }
+    b["total"] = sum(b.values())
+    b["unique_records"] = uniq
+    return b
+
+
+def step_flops(shape, t: int) -> dict:
+    R, H, W, dk, dv = shape.R, shape.H, shape.W, shape.dk, shape.dv
+    proj = R * H * 4 * W * dv * dk                       # S0 [k q] for 2W vectors
+    replay = R * H * W * (t - 1) * (4 * dk + 4 * dv)
+    epi = R * H * W * (2 * dk + 6 * dv)
+    return {"projection": proj, "total": proj + replay + epi}
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------ CPU baseline
+def _oracle_pair(args):
+    import oracle
+
+    S0, q, k, v, a, b, par = args
+    t0 = time.perf_counter()
+    oracle.full_state_episode(S0, q, k, v, a, b, par)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(shape, ep, n_pairs: int):
+    """Oracle (float64 full state per beam) on n_pairs (request, head) pairs, all steps."""
+    import multiprocessing as mp
+
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rng = np.random.default_rng(7)
+    pairs = [(int(rng.integers(shape.R)), int(rng.integers(shape.H))) for _ in range(n_pairs)]
+    W = shape.W
+    jobs = []
+    for (r, h) in pairs:
+        sl = slice(r * W, (r + 1) * W)
+        f = lambda key: bf16_bits_to_f32(ep[key][:, sl, h, :])
+        jobs.append((ep["S0"][r, h], f("q"), f("k"), f("v"), ep["alpha"][:, sl, h], ep["beta"][:, sl, h],
+                     ep["parents"][:, r, :]))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(min(cores, n_pairs)) as pool:
+        t0 = time.perf_counter()
+        per_pair = pool.map(_oracle_pair, jobs)
+        wall = time.perf_counter() - t0
+    beam_steps = W * shape.T * n_pairs / shape.H       # a beam-step covers all H heads
+    return {
+        "value": beam_steps / wall,
+        "unit": "beam-steps/s",
+        "cores": min(cores, n_pairs),
+        "kind": "oracle",
+        "sample": (f"{n_pairs} (request, head) pairs of {shape.name}, all {shape.T} steps, float64 full state "
+                   f"per beam; {wall:.1f} s wall, {sum(per_pair):.1f} s CPU; scaled by {shape.H} heads per "
+                   "beam-step"),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50, help="timed episodes")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed episodes")
+    ap.add_argument("--beams-per-block", type=int, default=0)
+    ap.add_argument("--cpu-pairs", type=int, default=64, help="(request, head) pairs the oracle runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests and heads would shard across GPUs with no exchange inside a step).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_beam_gdn_amd import Onela
+
+    shape = shape_of(3)
+    R, H, W, T, dk, dv = shape.R, shape.H, shape.W, shape.T, shape.dk, shape.dv
+    t_gen = time.perf_counter()
+    ep = make_episode(shape)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16) if a.dtype == np.uint16 else t).to(dev)
+
+    q = [up(ep["q"][t]) for t in range(T)]
+    k = [up(ep["k"][t]) for t in range(T)]
+    v = [up(ep["v"][t]) for t in range(T)]
+    al = [up(ep["alpha"][t]) for t in range(T)]
+    be = [up(ep["beta"][t]) for t in range(T)]
+    par = [None] + [up(ep["parents"][t].astype(np.int32)) for t in range(1, T)]
+    o = torch.empty((R * W, H, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    lay = Onela(R, H, dk, dv, W, T, stream=stream)
+    if args.beams_per_block:
+        lay.set_beams_per_block(args.beams_per_block)
+    for r in range(R):
+        lay.init_request(r, up(ep["S0"][r]))
+    reqs = list(range(R))
+
+    def episode(events=None):
+        for r in reqs:
+            lay.reset(r)
+        for t in range(T):
+            if events is not None:
+                events[t][0].record(stream)
+            lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t], o)
+            if events is not None:
+                events[t][1].record(stream)
+
+    for _ in range(args.warmup):
+        episode()
+    lay.sync()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        episode(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lay.sync()
+
+    per_t_ms = np.array([[evs[i][t][0].elapsed_time(evs[i][t][1]) for t in range(T)] for i in range(args.steps)])
+    med_t_us = np.median(per_t_ms, axis=0) * 1e3
+    mean_launch_s = per_t_ms.mean() * 1e-3
+    bytes_t = [step_bytes(shape, ep["parents"], t + 1) for t in range(T)]
+    flops_t = [step_flops(shape, t + 1) for t in range(T)]
+    bytes_per_launch = float(np.mean([b["total"] for b in bytes_t]))
+    achieved_gbs = bytes_per_launch / mean_launch_s / 1e9
+    proj_tflops = float(np.mean([f["projection"] for f in flops_t])) / mean_launch_s / 1e12
+
+    ms_per_step = wall / args.steps * 1e3
+    value = R * W * T / (wall / args.steps)
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "beam-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name,
+            "requests": R, "heads": H, "d_k": dk, "d_v": dv, "beam_width": W, "decode_steps": T,
+            "s0": "N(0, 0.05^2) float32 per head", "parents": "top W of 4W candidates per request",
+            "inputs": "bf16 q, k (L2-normalised), v; float32 alpha, beta",
+            "step": "one episode = host rewind + 5 decode steps of one GDN layer, one launch each",
+        },
+        "us_per_decode_step": ms_per_step * 1e3 / T,
+        "us_per_decode_step_by_depth": [round(float(x), 2) for x in med_t_us],
+        "kernel_us_mean": mean_launch_s * 1e6,
+        "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": KERNEL_NAME,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "mfma_projection": {
+            "achieved_tflops": proj_tflops,
+            "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": proj_tflops / BF16_PEAK_TFLOPS,
+            "note": "S0 projection flops of the fused launch over its whole duration (the launch is HBM-bound); "
+                    "issued MFMA work is 2x (split-bf16 S0)",
+        },
+        "input_generation_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)
+    lay.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,8 +125,9 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
                         const int32_t* parent_idx, float* o, float* delta_out);
 
 /* Rewind request `req` to step 0, keeping its S0 (the records of the old
- * episode become dead and are overwritten by the next one). Host-only, O(1),
- * except that the request's device error word is cleared on the stream. */
+ * episode become dead and are overwritten by the next one). Host-only and
+ * O(1): nothing is enqueued; a device error left by the old episode no
+ * longer counts. */
 onela_status onela_reset(onela_ctx* ctx, int32_t req);
 
 /* Wait for the stream. Returns ONELA_E_PARENT_RANGE if any request is

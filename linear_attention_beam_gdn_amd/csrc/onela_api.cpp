@@ -25,6 +25,8 @@ struct onela_ctx {
     std::vector<int32_t> steps;      // steps done per request; -1 = never initialised
     std::vector<char> poisoned;      // a bad parent index was reported
     std::vector<int32_t> err_host;
+    std::vector<int32_t> epoch;      // episode number per request; a device error word counts only
+                                     // if it carries the current one, so reset needs no device work
     int32_t beams_per_block = 0;     // 0 = automatic
     std::string last_error;
     uint64_t s0_bytes = 0, rec_bytes = 0, idx_bytes = 0;
@@ -51,7 +53,7 @@ onela_status drain(onela_ctx* ctx) {
                   hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(err)");
     for (int r = 0; r < ctx->cfg.max_requests; ++r)
-        if (ctx->err_host[r]) ctx->poisoned[r] = 1;
+        if (ctx->err_host[r] != 0 && ctx->err_host[r] == ctx->epoch[r]) ctx->poisoned[r] = 1;
     return ONELA_OK;
 }
 
@@ -125,6 +127,7 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
     ctx->steps.assign(R, -1);
     ctx->poisoned.assign(R, 0);
     ctx->err_host.assign(R, 0);
+    ctx->epoch.assign(R, 0);
     *out = ctx;
     return ONELA_OK;
 }
@@ -148,22 +151,18 @@ onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0) {
     uint16_t* planes = ctx->s0_planes + (size_t)req * c.num_heads * 2 * c.d_v * c.d_k;
     hipError_t e = onela::launch_init_s0(c.d_k, c.d_v, S0, planes, c.num_heads, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "init_s0 launch");
-    e = hipMemsetAsync(ctx->err + req, 0, 4, ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemsetAsync(err)");
     ctx->steps[req] = 0;
     ctx->poisoned[req] = 0;
-    ctx->err_host[req] = 0;
+    ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
     return ONELA_OK;
 }
 
 onela_status onela_reset(onela_ctx* ctx, int32_t req) {
     if (!ctx || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
-    hipError_t e = hipMemsetAsync(ctx->err + req, 0, 4, ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemsetAsync(err)");
     ctx->steps[req] = 0;
     ctx->poisoned[req] = 0;
-    ctx->err_host[req] = 0;
+    ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
     return ONELA_OK;
 }
 
@@ -224,6 +223,7 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         for (int i = 0; i < n; ++i) {
             p.slot[i] = reqs[i0 + i];
             p.t[i] = ctx->steps[reqs[i0 + i]] + 1;
+            p.epoch[i] = ctx->epoch[reqs[i0 + i]];
         }
         hipError_t e = onela::launch_step(c.d_k, c.d_v, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");

@@ -28,13 +28,14 @@ struct StepParams {
     float* rec_delta;           // [max_requests][H][T_max*W][DV]
     uint16_t* rec_k;            // [max_requests][H][T_max*W][DK]
     int32_t* anc;               // [2][max_requests][W][T_max] (ping-pong by step parity)
-    int32_t* err;               // [max_requests]
+    int32_t* err;               // [max_requests]: epoch of the last step that saw a bad parent
     int32_t H, W, T_max, max_requests;
     int32_t beams_per_block;    // multiple of kChunk, or >= W
     int32_t n_splits;           // ceil(W / beams_per_block)
     int32_t n_req;
     int32_t slot[kMaxReqPerLaunch];  // request id of call-local request i
     int32_t t[kMaxReqPerLaunch];     // step this launch performs for it (1-based)
+    int32_t epoch[kMaxReqPerLaunch]; // its episode number (> 0), written to err on a bad parent
 };
 
 // Returns hipErrorInvalidValue for unsupported (DK, DV).

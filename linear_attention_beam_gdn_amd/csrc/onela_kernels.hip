@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * (DV / 32)) void step_kernel(const StepParams p
             if (depth > 0) {
                 int par = p.parent[row0 + b];
                 if (par < 0 || par >= W) {        // reported through the error word
-                    p.err[slot] = 1;
+                    p.err[slot] = p.epoch[ri];
                     par = 0;
                 }
                 const int* src = anc_prev + (size_t)par * p.T_max;
