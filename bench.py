@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--beams-per-block", type=int, default=0)
     ap.add_argument("--cpu-pairs", type=int, default=64, help="(request, head) pairs the oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB first (reference for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -170,6 +172,13 @@ def main():
     import torch
 
     from linear_attention_beam_gdn_amd import Onela
+
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     shape = shape_of(3)
     R, H, W, T, dk, dv = shape.R, shape.H, shape.W, shape.T, shape.dk, shape.dv

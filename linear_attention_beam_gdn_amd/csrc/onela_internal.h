@@ -42,6 +42,6 @@ struct StepParams {
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
 bool step_supported(int dk, int dv);
-size_t step_lds_bytes(int dk, int T_max);
+size_t step_lds_bytes(int dk, int dv, int T_max);
 
 }  // namespace onela

@@ -4,22 +4,22 @@
 // kernel reuses the shared state across beams). A workgroup owns one
 // (request, head) pair and a range of beams, which it walks in chunks of
 // kChunk beams. For each chunk it
-//   A. stages k_t and q_t of the chunk's beams in LDS, appends k_t and
-//      alpha_t to the record store, and builds each beam's ancestry row from
-//      its parent's row (ids only; OneLA abstract: records are never moved);
+//   A. stages k_t and q_t of the chunk's beams in LDS and builds each beam's
+//      ancestry row from its parent's row (record ids only; OneLA abstract:
+//      records are never moved or copied);
 //   B. computes, per beam and ancestral record j, the dot products k_j . k_t
-//      and k_j . q_t (the only way the replay touches x; OneLA review,
-//      "Scope & Claims", paper Eq. 3), plus k_t . q_t;
+//      and k_j . q_t, the only way the replay touches x (OneLA review,
+//      "Scope & Claims": the recurrence right-multiplied by q_t and k_t,
+//      paper Eq. 3), plus k_t . q_t;
 //   C. projects the shared state once for all 2*kChunk vectors,
 //      P = S0 [k_t q_t], on the matrix cores (split-bf16: S0 = hi + lo);
-//   D. replays the ancestry in the MFMA accumulator registers,
-//      y <- alpha_j y + (k_j . x) delta_j, which leaves y = S_{t-1} x, then
-//      forms delta_t = beta (v - alpha y_k), o_t = alpha y_q + (k_t . q_t) delta_t
-//      (= S_t q_t) and appends delta_t.
+//   D. completes the replay in the MFMA accumulator registers, forms
+//      delta_t = beta (v - alpha y_k) and o_t = alpha y_q + (k_t . q_t) delta_t
+//      (= S_t q_t), and appends (alpha_t, delta_t, k_t).
 //
-// Wave w of the workgroup owns rows [32w, 32w+32) of d_v: its slice of S0
+// Wave w of the workgroup owns rows [16w, 16w+16) of d_v: its slice of S0
 // stays in registers as MFMA A-fragments for the whole beam loop, and every
-// step after the projection is row-separable, so no wave ever needs another
+// step after the projection is row-separable, so no wave needs another
 // wave's rows.
 #include "onela_internal.h"
 
@@ -27,7 +27,10 @@ namespace onela {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerWave = 16;     // d_v rows per wave (one 16x16x32 MFMA tile row block)
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -38,35 +41,46 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
     return u >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// sum of the 8 bf16 products of a and b, plus acc, in fp32 (packed dot2)
 __device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc) {
-    acc = fmaf(bf_lo(a.x), bf_lo(b.x), acc);
-    acc = fmaf(bf_hi(a.x), bf_hi(b.x), acc);
-    acc = fmaf(bf_lo(a.y), bf_lo(b.y), acc);
-    acc = fmaf(bf_hi(a.y), bf_hi(b.y), acc);
-    acc = fmaf(bf_lo(a.z), bf_lo(b.z), acc);
-    acc = fmaf(bf_hi(a.z), bf_hi(b.z), acc);
-    acc = fmaf(bf_lo(a.w), bf_lo(b.w), acc);
-    acc = fmaf(bf_hi(a.w), bf_hi(b.w), acc);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.z), as_bf16x2(b.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.w), as_bf16x2(b.w), acc, false);
     return acc;
+}
+
+// Workgroup barrier that orders LDS only. Inside one step launch no thread
+// reads global memory another thread of the launch wrote (records of this
+// step are appended at ids no one reads before the next launch), so the
+// barriers need not wait for outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------------------
 // S0 (float32, row-major [H][DV][DK]) -> two bf16 planes hi, lo with
 // hi = rne(S0), lo = rne(S0 - hi), stored in the order the step kernel loads
 // its MFMA A-fragments: fragment f = (w*KS + kk)*64 + lane holds the 8 values
-// S0[32w + lane%32][16kk + 8*(lane/32) + 0..7].
+// S0[16w + lane%16][32kk + 8*(lane/16) + 0..7].
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void init_s0_kernel(const float* __restrict__ S0,
                                                       uint16_t* __restrict__ planes, int H) {
-    constexpr int KS = DK / 16;
+    constexpr int KS = DK / 32;
     constexpr int NFRAG = DV * DK / 8;
     const int f = blockIdx.x * 256 + threadIdx.x;
     if (f >= H * NFRAG) return;
     const int h = f / NFRAG, fi = f % NFRAG;
     const int lane = fi & 63, wk = fi >> 6;
     const int w = wk / KS, kk = wk % KS;
-    const int m = 32 * w + (lane & 31);
-    const int kb = 16 * kk + 8 * (lane >> 5);
+    const int m = kRowsPerWave * w + (lane & 15);
+    const int kb = 32 * kk + 8 * (lane >> 4);
     const float* src = S0 + ((size_t)h * DV + m) * DK + kb;
     const float4 x0 = *reinterpret_cast<const float4*>(src);
     const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
@@ -85,35 +99,43 @@ __global__ __launch_bounds__(256) void init_s0_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-template <int DK>
-__host__ __device__ constexpr int xs_row() { return DK + 8; }  // padded LDS row (bf16), breaks bank aliasing
+template <int DV>
+__host__ __device__ constexpr int step_threads() { return 64 * (DV / kRowsPerWave); }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DV / 32)) void step_kernel(const StepParams p) {
+__global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(const StepParams p) {
     constexpr int CH = kChunk;
-    constexpr int NW = DV / 32;        // waves; wave w owns d_v rows [32w, 32w+32)
+    constexpr int NW = DV / kRowsPerWave;
     constexpr int NT = 64 * NW;
-    constexpr int KS = DK / 16;        // MFMA k-steps
-    constexpr int NB = CH / 32;        // 32-beam column groups per chunk
-    constexpr int XS = xs_row<DK>();
-    constexpr int TPB = NT / CH;       // threads per beam in the dot-product phase
-    constexpr int EPT = DK / TPB;      // key elements per thread there
-    static_assert(DV % 32 == 0 && DK % 16 == 0, "tile shape");
-    static_assert(TPB >= 1 && EPT % 8 == 0, "dot-product split");
+    constexpr int KS = DK / 32;        // MFMA k-steps
+    constexpr int NG = CH / 32;        // 32-beam groups per chunk
+    constexpr int XS = DK + 8;         // padded LDS row (bf16 elements): breaks bank aliasing
+    constexpr int MT = CH / 16;        // 16-beam tiles per chunk
+    constexpr int TPQ = NT / CH;       // threads per beam for k_t . q_t
+    constexpr int EQ = DK / TPQ;       // elements per thread there
+    static_assert(TPQ >= 1 && EQ % 8 == 0, "k_t . q_t split");
+    static_assert((2 * CH * (DK / 8)) % NT == 0 && (CH * (DV / 8)) % NT == 0, "whole stream loads per thread");
+    constexpr int DBD = 4;             // depths whose delta gathers are in flight together
+    constexpr int VS = DV + 8;         // padded LDS row of v (bf16 elements)
+    static_assert(DV % kRowsPerWave == 0 && DK % 32 == 0, "tile shape");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     const int MS = p.T_max > 1 ? p.T_max - 1 : 1;                  // ancestry depth capacity
-    float4* coef_s = reinterpret_cast<float4*>(lds_raw);            // [CH][MS] {k_j.k_t, k_j.q_t, alpha_j, rid}
+    float4* coef_s = reinterpret_cast<float4*>(lds_raw);            // [MS][CH] {k_j.k_t, k_j.q_t, alpha_j, rid}
     uint16_t* xs = reinterpret_cast<uint16_t*>(coef_s + CH * MS);   // [2*CH][XS]: k rows then q rows
-    int* anc_s = reinterpret_cast<int*>(xs + 2 * CH * XS);          // [CH][MS]
-    float* kq_s = reinterpret_cast<float*>(anc_s + CH * MS);        // [CH]
+    uint16_t* vs = xs + 2 * CH * XS;                                // [CH][VS]: v rows
+    int* anc_s = reinterpret_cast<int*>(vs + CH * VS);              // [MS][CH] record ids, oldest first
+    float* kq_s = reinterpret_cast<float*>(anc_s + CH * MS);        // [CH]: k_t . q_t
+    float* at_s = kq_s + CH;                                        // [CH]: alpha_t
+    float* bt_s = at_s + CH;                                        // [CH]: beta_t
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
     // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that
-    // the beam splits of one (request, head) land on one XCD and share its L2.
+    // the beam splits of one (request, head), and the heads of one request,
+    // land on one XCD and share its L2.
     int L = blockIdx.x;
     const int nblk = gridDim.x;
     if ((nblk & 7) == 0) L = (L & 7) * (nblk >> 3) + (L >> 3);
@@ -129,9 +151,23 @@ __global__ __launch_bounds__(64 * (DV / 32)) void step_kernel(const StepParams p
     const int b_end = min(W, b_begin + p.beams_per_block);
     if (b_begin >= b_end) return;
 
+    // Uniform 64-bit bases of this (request, head); every per-lane offset from
+    // them is a 32-bit int (the host rejects shapes where that could overflow).
     const size_t pair_id = (size_t)slot * H + h;
     const size_t rec0 = pair_id * (size_t)p.T_max * W;            // record 0 of this (request, head)
-    const size_t row0 = (size_t)ri * W;                            // first input row of this request
+    const size_t in0 = (size_t)ri * W * H + h;                     // input row of (beam 0, head h)
+    const int HK = H * DK, HV = H * DV;                            // input row strides between beams
+    const uint16_t* kin = p.k + in0 * DK;
+    const uint16_t* qin = p.q + in0 * DK;
+    const uint16_t* vin = p.v + in0 * DV;
+    const float* ain = p.alpha + in0;
+    const float* bin = p.beta + in0;
+    float* oout = p.o + in0 * DV;
+    float* dout = p.delta_out ? p.delta_out + in0 * DV : nullptr;
+    const int* parin = depth > 0 ? p.parent + (size_t)ri * W : nullptr;
+    float* ralpha = p.rec_alpha + rec0;                            // record r: ralpha[r]
+    float* rdelta = p.rec_delta + rec0 * DV;                       // record r: rdelta + r*DV
+    uint16_t* rkey = p.rec_k + rec0 * DK;                          // record r: rkey + r*DK
     const int* anc_prev = p.anc + ((size_t)((t - 1) & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* anc_next = p.anc + ((size_t)(t & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
 
@@ -146,144 +182,271 @@ __global__ __launch_bounds__(64 * (DV / 32)) void step_kernel(const StepParams p
         }
     }
 
+    // The replay is linear in the records, so instead of the sequential
+    //   y <- alpha_j y + (k_j . x) delta_j      (j = oldest .. newest)
+    // the kernel forms
+    //   y = (prod_j alpha_j) S0 x + sum_j (k_j . x) (prod_{i>j} alpha_i) delta_j,
+    // which makes the gathers of all depths independent: key gathers of
+    // several depths are in flight together, and the newest block of delta
+    // gathers is in flight during the projection MFMAs.
+    const int n16 = lane & 15;                   // MFMA column within a 16-wide tile
+    const int quad = lane >> 4;                  // which 4 rows of the wave's 16 this lane holds
+    const int rbase = wave * kRowsPerWave + quad * 4;
+    // Streaming inputs of a chunk (k_t, q_t, v_t, alpha_t, beta_t, parents) are
+    // loaded one chunk ahead, so they are in flight while the previous chunk
+    // gathers records and runs its MFMAs.
+    constexpr int SEG = DK / 8;                          // 16-byte pieces per k/q row
+    constexpr int XITER = (2 * CH * SEG + NT - 1) / NT;
+    constexpr int VSEG = DV / 8;                         // 16-byte pieces per v row
+    constexpr int VITER = (CH * VSEG + NT - 1) / NT;
+    u32x4 xv[XITER], vv[VITER];         // plain vector type: stays in registers
+    float a_new = 0.f, b_new = 0.f;
+    int par = 0;
+    // Every gather and stream load below is issued unconditionally, from a
+    // clamped address that is always inside its buffer (results for beams
+    // past the end of the range are never used): with no branch around a
+    // load, the compiler knows exactly how many loads are younger than the
+    // one it waits for, and waits for no more than that.
+    const int* parsrc = depth > 0 ? parin : reinterpret_cast<const int*>(ain);   // any valid int source at t = 1
+    auto load_stream = [&](int cs) __attribute__((always_inline)) {
+        const int last = min(CH, b_end - cs) - 1;
+#pragma unroll
+        for (int it = 0; it < XITER; ++it) {
+            const int idx = tid + it * NT;
+            const int row = idx / SEG, seg = idx % SEG;
+            const bool is_k = row < CH;
+            const int bl = min(is_k ? row : row - CH, last);
+            xv[it] = *reinterpret_cast<const u32x4*>((is_k ? kin : qin) + (cs + bl) * HK + seg * 8);
+        }
+#pragma unroll
+        for (int it = 0; it < VITER; ++it) {
+            const int idx = tid + it * NT;
+            const int bl = min(idx / VSEG, last), seg = idx % VSEG;
+            vv[it] = *reinterpret_cast<const u32x4*>(vin + (cs + bl) * HV + seg * 8);
+        }
+        const int bq = min(tid, last);
+        a_new = ain[(cs + bq) * H];
+        b_new = bin[(cs + bq) * H];
+        par = parsrc[cs + bq];
+    };
+    load_stream(b_begin);
+
     for (int c0 = b_begin; c0 < b_end; c0 += CH) {
         const int nb = min(CH, b_end - c0);
 
-        // ---- A. stage k_t, q_t; append k_t, alpha_t; ancestry rows --------
-        constexpr int SEG = DK / 8;                      // 16-byte pieces per row
-        for (int idx = tid; idx < 2 * CH * SEG; idx += NT) {
-            const int row = idx / SEG, seg = idx % SEG;
-            const bool is_k = row < CH;
-            const int bl = is_k ? row : row - CH;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (bl < nb) {
-                const size_t in = ((row0 + c0 + bl) * H + h) * DK + seg * 8;
-                val = *reinterpret_cast<const uint4*>((is_k ? p.k : p.q) + in);
-                if (is_k)
-                    *reinterpret_cast<uint4*>(p.rec_k + (rec0 + (size_t)depth * W + c0 + bl) * DK + seg * 8) = val;
+        // ---- A. stage k_t, q_t, v_t, alpha_t, beta_t; ancestry rows ---------
+        const bool beam_thread = tid < nb;                   // one thread per beam of the chunk
+        if (beam_thread && depth > 0) {
+            if (par < 0 || par >= W) {                       // reported through the error word
+                p.err[slot] = p.epoch[ri];
+                par = 0;
             }
-            *reinterpret_cast<uint4*>(xs + row * XS + seg * 8) = val;
+            const int* src = anc_prev + par * p.T_max;
+            for (int j = 0; j + 1 < depth; ++j) anc_s[j * CH + tid] = src[j];
+            anc_s[(depth - 1) * CH + tid] = (depth - 1) * W + par;   // parent's own record of step t-1
         }
-        for (int bl = tid; bl < nb; bl += NT) {
-            const int b = c0 + bl;
-            p.rec_alpha[rec0 + (size_t)depth * W + b] = p.alpha[(row0 + b) * H + h];
-            if (depth > 0) {
-                int par = p.parent[row0 + b];
-                if (par < 0 || par >= W) {        // reported through the error word
-                    p.err[slot] = p.epoch[ri];
-                    par = 0;
-                }
-                const int* src = anc_prev + (size_t)par * p.T_max;
-                for (int j = 0; j + 1 < depth; ++j) anc_s[bl * MS + j] = src[j];
-                anc_s[bl * MS + depth - 1] = (depth - 1) * W + par;   // parent's own record of step t-1
-                if (h == 0)   // one head writes the request's new index rows
-                    for (int j = 0; j < depth; ++j) anc_next[(size_t)b * p.T_max + j] = anc_s[bl * MS + j];
+#pragma unroll
+        for (int it = 0; it < XITER; ++it) {
+            const int idx = tid + it * NT;
+            if (idx < 2 * CH * SEG) {
+                const int row = idx / SEG, seg = idx % SEG;
+                *reinterpret_cast<u32x4*>(xs + row * XS + seg * 8) = xv[it];
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < VITER; ++it) {
+            const int idx = tid + it * NT;
+            if (idx < CH * VSEG) {
+                const int bl = idx / VSEG, seg = idx % VSEG;
+                *reinterpret_cast<u32x4*>(vs + bl * VS + seg * 8) = vv[it];
+            }
+        }
+        if (beam_thread) {
+            at_s[tid] = a_new;
+            bt_s[tid] = b_new;
+        }
+        lds_barrier();
 
-        // ---- B. dot products of the ancestral keys with k_t and q_t -------
-        {
-            const int bl = tid / TPB, part = tid % TPB;
-            if (bl < nb) {
-                uint4 kt[EPT / 8], qt[EPT / 8];
+        // ---- B. k_j . k_t and k_j . q_t for every ancestral record j -------
+        // On the matrix cores: for a tile of 16 beams and one depth, the A
+        // operand is the 16 ancestral keys, gathered from the record store
+        // straight into A-fragments, and B holds the same beams' k_t (or q_t)
+        // columns from LDS; the wanted dot products are the diagonal of the
+        // 16x16 product, whose element (i, i) sits in lane i + 16*(i/4),
+        // register i%4. Loads leave in this order: key gathers, delta gathers
+        // (used in D), the next chunk's streaming inputs; the counter of
+        // outstanding loads retires in order, so each wait below covers only
+        // what it needs.
+        const int n_units = MT * depth;
+        const bool diag = (n16 >> 2) == quad;
+        bf16x8 af[2][KS];
+        int rid[2];
+        float aj[2];
+        auto issue_units = [&](int u0) __attribute__((always_inline)) {            // units u0 and u0 + NW of this wave
 #pragma unroll
-                for (int s = 0; s < EPT / 8; ++s) {
-                    kt[s] = *reinterpret_cast<const uint4*>(xs + bl * XS + part * EPT + s * 8);
-                    qt[s] = *reinterpret_cast<const uint4*>(xs + (CH + bl) * XS + part * EPT + s * 8);
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int u = u0 + h2 * NW;
+                const int m = u % MT, j = u / MT;
+                const int bl = m * 16 + n16;
+                rid[h2] = (u < n_units && bl < nb) ? anc_s[j * CH + bl] : 0;
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    af[h2][kk] = *reinterpret_cast<const bf16x8*>(rkey + rid[h2] * DK + kk * 32 + quad * 8);
+                aj[h2] = ralpha[rid[h2]];
+            }
+        };
+        auto consume_units = [&](int u0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int u = u0 + h2 * NW;
+                if (u >= n_units) break;                     // uniform across the wave
+                const int m = u % MT, j = u / MT;
+                f32x4 dk4 = f32x4{0.f, 0.f, 0.f, 0.f}, dq4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    const int koff = kk * 32 + quad * 8;
+                    const bf16x8 bk = *reinterpret_cast<const bf16x8*>(xs + (m * 16 + n16) * XS + koff);
+                    const bf16x8 bq = *reinterpret_cast<const bf16x8*>(xs + (CH + m * 16 + n16) * XS + koff);
+                    dk4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h2][kk], bk, dk4, 0, 0, 0);
+                    dq4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h2][kk], bq, dq4, 0, 0, 0);
                 }
-                float kq = 0.f;
-#pragma unroll
-                for (int s = 0; s < EPT / 8; ++s) kq = dot8(kt[s], qt[s], kq);
-#pragma unroll
-                for (int m = 1; m < TPB; m <<= 1) kq += __shfl_xor(kq, m, 64);
-                if (part == 0) kq_s[bl] = kq;
-                for (int j = 0; j < depth; ++j) {
-                    const int r = anc_s[bl * MS + j];
-                    const uint4* kj = reinterpret_cast<const uint4*>(p.rec_k + (rec0 + r) * DK + part * EPT);
-                    float dk = 0.f, dq = 0.f;
-#pragma unroll
-                    for (int s = 0; s < EPT / 8; ++s) {
-                        const uint4 kv = kj[s];
-                        dk = dot8(kv, kt[s], dk);
-                        dq = dot8(kv, qt[s], dq);
-                    }
-#pragma unroll
-                    for (int m = 1; m < TPB; m <<= 1) {
-                        dk += __shfl_xor(dk, m, 64);
-                        dq += __shfl_xor(dq, m, 64);
-                    }
-                    if (part == 0) coef_s[bl * MS + j] = make_float4(dk, dq, p.rec_alpha[rec0 + r], __int_as_float(r));
+                const int bl = m * 16 + n16;
+                if (diag && bl < nb) {
+                    const int r = n16 & 3;
+                    const float dk = r == 0 ? dk4[0] : r == 1 ? dk4[1] : r == 2 ? dk4[2] : dk4[3];
+                    const float dq = r == 0 ? dq4[0] : r == 1 ? dq4[1] : r == 2 ? dq4[2] : dq4[3];
+                    coef_s[j * CH + bl] = make_float4(dk, dq, aj[h2], __int_as_float(rid[h2]));
                 }
             }
+        };
+        issue_units(wave);
+
+        // The newest DBD ancestral deltas of every beam this lane replays in D.
+        float4 dd[NG][2][DBD];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int bl = g * 32 + u2 * 16 + n16;
+#pragma unroll
+                for (int u = 0; u < DBD; ++u) {
+                    const int j = depth - 1 - u;
+                    const int r = (bl < nb && j >= 0) ? anc_s[j * CH + bl] : 0;
+                    dd[g][u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
+                }
+            }
+
+        if (c0 + CH < b_end) load_stream(c0 + CH);     // next chunk's streaming inputs
+
+        consume_units(wave);
+        for (int u0 = wave + 2 * NW; u0 < n_units; u0 += 2 * NW) {   // depths beyond 2*NW/MT
+            issue_units(u0);
+            consume_units(u0);
+        }
+        {   // k_t . q_t on the vector units, from LDS
+            const int bl = tid / TPQ, part = tid % TPQ;
+            const uint16_t* kt_s = xs + bl * XS + part * EQ;
+            const uint16_t* qt_s = xs + (CH + bl) * XS + part * EQ;
+            float kq = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < EQ / 8; ++s2)
+                kq = dot8(*reinterpret_cast<const uint4*>(kt_s + s2 * 8), *reinterpret_cast<const uint4*>(qt_s + s2 * 8), kq);
+#pragma unroll
+            for (int m = 1; m < TPQ; m <<= 1) kq += __shfl_xor(kq, m, 64);
+            if (part == 0 && bl < nb) kq_s[bl] = kq;
         }
 
-        __syncthreads();   // coef_s / kq_s complete
+        lds_barrier();   // coef_s / kq_s complete
 
         // ---- C + D, one 32-beam group at a time ------------------------------
-        // C: y_k = S0 k_t, y_q = S0 q_t for the group's 32 beams on the matrix
-        //    cores (S0 = hi + lo, both bf16, fp32 accumulation).
-        // D: replay, epilogue and append. Accumulator register 4*rr + e of
-        //    lane l holds row 8*rr + 4*(l/32) + e (of this wave's 32) for
-        //    column (beam) l%32.
-        const int rbase = wave * 32 + (lane >> 5) * 4;
+        // Lane l handles beams g*32 + l%16 and g*32 + 16 + l%16 of the chunk
+        // and rows rbase .. rbase+3: the 16x16 MFMA accumulator register i of
+        // lane l holds row 4*(l/16) + i (of the wave's 16) for column l%16.
 #pragma unroll
-        for (int g = 0; g < NB; ++g) {
-            const int bl = g * 32 + (lane & 31);
-            f32x16 yk = f32x16{}, yq = f32x16{};
+        for (int g = 0; g < NG; ++g) {
+            f32x4 acc[4];                  // tiles: k of beams +0..15, k +16..31, q +0..15, q +16..31
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const int koff = kk * 16 + (lane >> 5) * 8;
-                const bf16x8 bk = *reinterpret_cast<const bf16x8*>(xs + bl * XS + koff);
-                const bf16x8 bq = *reinterpret_cast<const bf16x8*>(xs + (CH + bl) * XS + koff);
-                yk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[kk], bk, yk, 0, 0, 0);
-                yq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[kk], bq, yq, 0, 0, 0);
-                yk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[kk], bk, yk, 0, 0, 0);
-                yq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[kk], bq, yq, 0, 0, 0);
-            }
-            if (bl < nb) {
-                for (int j = 0; j < depth; ++j) {
-                    const float4 c = coef_s[bl * MS + j];
-                    const float* dj = p.rec_delta + (rec0 + __float_as_int(c.w)) * DV + rbase;
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const float4 d = *reinterpret_cast<const float4*>(dj + 8 * rr);
-                        yk[4 * rr + 0] = fmaf(c.z, yk[4 * rr + 0], c.x * d.x);
-                        yk[4 * rr + 1] = fmaf(c.z, yk[4 * rr + 1], c.x * d.y);
-                        yk[4 * rr + 2] = fmaf(c.z, yk[4 * rr + 2], c.x * d.z);
-                        yk[4 * rr + 3] = fmaf(c.z, yk[4 * rr + 3], c.x * d.w);
-                        yq[4 * rr + 0] = fmaf(c.z, yq[4 * rr + 0], c.y * d.x);
-                        yq[4 * rr + 1] = fmaf(c.z, yq[4 * rr + 1], c.y * d.y);
-                        yq[4 * rr + 2] = fmaf(c.z, yq[4 * rr + 2], c.y * d.z);
-                        yq[4 * rr + 3] = fmaf(c.z, yq[4 * rr + 3], c.y * d.w);
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int col = (ct >= 2 ? CH : 0) + g * 32 + (ct & 1) * 16 + n16;
+                    const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(xs + col * XS + kk * 32 + quad * 8);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[kk], bfr, acc[ct], 0, 0, 0);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[kk], bfr, acc[ct], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep B-fragment reads next to their k-step
+            }
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int bl = g * 32 + u2 * 16 + n16;
+                if (bl >= nb) continue;
+                // newest record first: w_j = (k_j . x) * prod_{i>j} alpha_i
+                f32x4 zk = f32x4{0.f, 0.f, 0.f, 0.f}, zq = f32x4{0.f, 0.f, 0.f, 0.f};
+                float sfx = 1.f;
+                for (int jt = depth - 1; jt >= 0; jt -= DBD) {
+                    if (jt != depth - 1) {                           // older blocks (depth > DBD)
+#pragma unroll
+                        for (int u = 0; u < DBD; ++u)
+                            if (jt - u >= 0)
+                                dd[g][u2][u] = *reinterpret_cast<const float4*>(
+                                    rdelta + anc_s[(jt - u) * CH + bl] * DV + rbase);
+                    }
+#pragma unroll
+                    for (int u = 0; u < DBD; ++u) {
+                        if (jt - u >= 0) {
+                            const float4 c = coef_s[(jt - u) * CH + bl];
+                            const float4 dv4 = dd[g][u2][u];
+                            const float wk = c.x * sfx, wq = c.y * sfx;
+                            sfx *= c.z;
+                            zk[0] = fmaf(wk, dv4.x, zk[0]);
+                            zk[1] = fmaf(wk, dv4.y, zk[1]);
+                            zk[2] = fmaf(wk, dv4.z, zk[2]);
+                            zk[3] = fmaf(wk, dv4.w, zk[3]);
+                            zq[0] = fmaf(wq, dv4.x, zq[0]);
+                            zq[1] = fmaf(wq, dv4.y, zq[1]);
+                            zq[2] = fmaf(wq, dv4.z, zq[2]);
+                            zq[3] = fmaf(wq, dv4.w, zq[3]);
+                        }
                     }
                 }
+                // sfx is now the product of alpha over the whole history
+                const f32x4 yk = acc[u2] * sfx + zk, yq = acc[2 + u2] * sfx + zq;
                 const int b = c0 + bl;
-                const size_t row = (row0 + b) * H + h;
-                const float at = p.alpha[row], bt = p.beta[row], kq = kq_s[bl];
-                const uint16_t* vp = p.v + row * DV + rbase;
-                float* op = p.o + row * DV + rbase;
-                float* rp = p.rec_delta + (rec0 + (size_t)depth * W + b) * DV + rbase;
-                float* dp = p.delta_out ? p.delta_out + row * DV + rbase : nullptr;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const uint2 vb = *reinterpret_cast<const uint2*>(vp + 8 * rr);
-                    float4 d, o;
-                    d.x = bt * (bf_lo(vb.x) - at * yk[4 * rr + 0]);
-                    d.y = bt * (bf_hi(vb.x) - at * yk[4 * rr + 1]);
-                    d.z = bt * (bf_lo(vb.y) - at * yk[4 * rr + 2]);
-                    d.w = bt * (bf_hi(vb.y) - at * yk[4 * rr + 3]);
-                    o.x = fmaf(at, yq[4 * rr + 0], kq * d.x);
-                    o.y = fmaf(at, yq[4 * rr + 1], kq * d.y);
-                    o.z = fmaf(at, yq[4 * rr + 2], kq * d.z);
-                    o.w = fmaf(at, yq[4 * rr + 3], kq * d.w);
-                    *reinterpret_cast<float4*>(op + 8 * rr) = o;
-                    *reinterpret_cast<float4*>(rp + 8 * rr) = d;
-                    if (dp) *reinterpret_cast<float4*>(dp + 8 * rr) = d;
-                }
+                const float kq = kq_s[bl], a = at_s[bl], bb = bt_s[bl];
+                const uint2 vb = *reinterpret_cast<const uint2*>(vs + bl * VS + rbase);
+                float4 d, o;
+                d.x = bb * (bf_lo(vb.x) - a * yk[0]);
+                d.y = bb * (bf_hi(vb.x) - a * yk[1]);
+                d.z = bb * (bf_lo(vb.y) - a * yk[2]);
+                d.w = bb * (bf_hi(vb.y) - a * yk[3]);
+                o.x = fmaf(a, yq[0], kq * d.x);
+                o.y = fmaf(a, yq[1], kq * d.y);
+                o.z = fmaf(a, yq[2], kq * d.z);
+                o.w = fmaf(a, yq[3], kq * d.w);
+                *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
+                *reinterpret_cast<float4*>(rdelta + (depth * W + b) * DV + rbase) = d;
+                if (dout) *reinterpret_cast<float4*>(dout + b * HV + rbase) = d;
             }
         }
-        __syncthreads();   // LDS is reused by the next chunk
+
+        // ---- append k_t, alpha_t and the new index rows (after every gather) -
+#pragma unroll
+        for (int it = 0; it < XITER; ++it) {
+            const int idx = tid + it * NT;
+            const int row = idx / SEG, seg = idx % SEG;
+            if (idx < 2 * CH * SEG && row < nb)
+                *reinterpret_cast<uint4*>(rkey + (depth * W + c0 + row) * DK + seg * 8) =
+                    *reinterpret_cast<const uint4*>(xs + row * XS + seg * 8);
+        }
+        if (beam_thread) {
+            const int b = c0 + tid;
+            ralpha[depth * W + b] = at_s[tid];              // a_new already holds the next chunk's
+            if (h == 0)   // one head writes the request's new index rows
+                for (int j = 0; j < depth; ++j) anc_next[b * p.T_max + j] = anc_s[j * CH + tid];
+        }
+        lds_barrier();   // LDS is reused by the next chunk
     }
 }
 
@@ -296,22 +459,26 @@ hipError_t launch_init_t(const float* S0, uint16_t* planes, int H, hipStream_t s
 
 template <int DK, int DV>
 hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
-    const size_t lds = step_lds_bytes(DK, p.T_max);
+    const size_t lds = step_lds_bytes(DK, DV, p.T_max);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int nblk = p.n_req * p.H * p.n_splits;
-    hipLaunchKernelGGL((step_kernel<DK, DV>), dim3(nblk), dim3(64 * (DV / 32)), lds, s, p);
+    hipLaunchKernelGGL((step_kernel<DK, DV>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t step_lds_bytes(int dk, int T_max) {
+size_t step_lds_bytes(int dk, int dv, int T_max) {
     const size_t ms = T_max > 1 ? (size_t)T_max - 1 : 1;
-    return kChunk * ms * 16 + 2 * kChunk * (size_t)(dk + 8) * 2 + kChunk * ms * 4 + kChunk * 4;
+    return kChunk * ms * 16                       // coef_s
+           + 2 * kChunk * (size_t)(dk + 8) * 2    // xs
+           + kChunk * (size_t)(dv + 8) * 2        // vs
+           + kChunk * ms * 4                      // anc_s
+           + 3 * kChunk * 4;                      // kq_s, at_s, bt_s
 }
 
 bool step_supported(int dk, int dv) {
