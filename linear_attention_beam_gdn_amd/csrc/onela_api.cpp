@@ -58,12 +58,12 @@ onela_status drain(onela_ctx* ctx) {
 }
 
 int auto_beams_per_block(const onela_ctx* ctx, int n_pairs) {
-    // Enough workgroups to give each of the 256 CUs several, while keeping
-    // as many beams as possible per workgroup (S0 stays in registers across
-    // them).
+    // Two workgroups fit on each of the 256 CUs: aim for at least 512 of
+    // them, while keeping as many beams as possible per workgroup (its S0
+    // slice stays in registers across them).
     const int W = ctx->cfg.beam_width;
     const int chunks = (W + onela::kChunk - 1) / onela::kChunk;
-    int splits = std::max(1, std::min(chunks, (1024 + n_pairs - 1) / n_pairs));
+    int splits = std::max(1, std::min(chunks, (512 + n_pairs - 1) / n_pairs));
     const int per = (chunks + splits - 1) / splits;
     return per * onela::kChunk;
 }

@@ -103,7 +103,7 @@ template <int DV>
 __host__ __device__ constexpr int step_threads() { return 64 * (DV / kRowsPerWave); }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(const StepParams p) {
+__global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
     constexpr int CH = kChunk;
     constexpr int NW = DV / kRowsPerWave;
     constexpr int NT = 64 * NW;
@@ -115,7 +115,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     constexpr int EQ = DK / TPQ;       // elements per thread there
     static_assert(TPQ >= 1 && EQ % 8 == 0, "k_t . q_t split");
     static_assert((2 * CH * (DK / 8)) % NT == 0 && (CH * (DV / 8)) % NT == 0, "whole stream loads per thread");
-    constexpr int DBD = 4;             // depths whose delta gathers are in flight together
+    constexpr int DBD = 2;             // depths whose delta gathers are in flight together
+    constexpr int UPP = 2;             // dot-product units per wave whose key gathers are in flight together
     constexpr int VS = DV + 8;         // padded LDS row of v (bf16 elements)
     static_assert(DV % kRowsPerWave == 0 && DK % 32 == 0, "tile shape");
 
@@ -192,9 +193,9 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     const int n16 = lane & 15;                   // MFMA column within a 16-wide tile
     const int quad = lane >> 4;                  // which 4 rows of the wave's 16 this lane holds
     const int rbase = wave * kRowsPerWave + quad * 4;
-    // Streaming inputs of a chunk (k_t, q_t, v_t, alpha_t, beta_t, parents) are
-    // loaded one chunk ahead, so they are in flight while the previous chunk
-    // gathers records and runs its MFMAs.
+    // Streaming inputs of a chunk: k_t, q_t, v_t, alpha_t, beta_t, parents.
+    // (Two workgroups share a CU, 128 registers per lane each; latency is
+    // hidden by the other workgroup rather than by prefetching in registers.)
     constexpr int SEG = DK / 8;                          // 16-byte pieces per k/q row
     constexpr int XITER = (2 * CH * SEG + NT - 1) / NT;
     constexpr int VSEG = DV / 8;                         // 16-byte pieces per v row
@@ -229,12 +230,12 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         b_new = bin[(cs + bq) * H];
         par = parsrc[cs + bq];
     };
-    load_stream(b_begin);
 
     for (int c0 = b_begin; c0 < b_end; c0 += CH) {
         const int nb = min(CH, b_end - c0);
 
         // ---- A. stage k_t, q_t, v_t, alpha_t, beta_t; ancestry rows ---------
+        load_stream(c0);
         const bool beam_thread = tid < nb;                   // one thread per beam of the chunk
         if (beam_thread && depth > 0) {
             if (par < 0 || par >= W) {                       // reported through the error word
@@ -273,18 +274,15 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         // straight into A-fragments, and B holds the same beams' k_t (or q_t)
         // columns from LDS; the wanted dot products are the diagonal of the
         // 16x16 product, whose element (i, i) sits in lane i + 16*(i/4),
-        // register i%4. Loads leave in this order: key gathers, delta gathers
-        // (used in D), the next chunk's streaming inputs; the counter of
-        // outstanding loads retires in order, so each wait below covers only
-        // what it needs.
+        // register i%4.
         const int n_units = MT * depth;
         const bool diag = (n16 >> 2) == quad;
-        bf16x8 af[2][KS];
-        int rid[2];
-        float aj[2];
-        auto issue_units = [&](int u0) __attribute__((always_inline)) {            // units u0 and u0 + NW of this wave
+        bf16x8 af[UPP][KS];
+        int rid[UPP];
+        float aj[UPP];
+        auto issue_units = [&](int u0) __attribute__((always_inline)) {   // units u0, u0 + NW, ... of this wave
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
+            for (int h2 = 0; h2 < UPP; ++h2) {
                 const int u = u0 + h2 * NW;
                 const int m = u % MT, j = u / MT;
                 const int bl = m * 16 + n16;
@@ -297,7 +295,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         };
         auto consume_units = [&](int u0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
+            for (int h2 = 0; h2 < UPP; ++h2) {
                 const int u = u0 + h2 * NW;
                 if (u >= n_units) break;                     // uniform across the wave
                 const int m = u % MT, j = u / MT;
@@ -321,25 +319,9 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         };
         issue_units(wave);
 
-        // The newest DBD ancestral deltas of every beam this lane replays in D.
-        float4 dd[NG][2][DBD];
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int u2 = 0; u2 < 2; ++u2) {
-                const int bl = g * 32 + u2 * 16 + n16;
-#pragma unroll
-                for (int u = 0; u < DBD; ++u) {
-                    const int j = depth - 1 - u;
-                    const int r = (bl < nb && j >= 0) ? anc_s[j * CH + bl] : 0;
-                    dd[g][u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
-                }
-            }
-
-        if (c0 + CH < b_end) load_stream(c0 + CH);     // next chunk's streaming inputs
 
         consume_units(wave);
-        for (int u0 = wave + 2 * NW; u0 < n_units; u0 += 2 * NW) {   // depths beyond 2*NW/MT
+        for (int u0 = wave + UPP * NW; u0 < n_units; u0 += UPP * NW) {   // deeper histories
             issue_units(u0);
             consume_units(u0);
         }
@@ -362,8 +344,21 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         // Lane l handles beams g*32 + l%16 and g*32 + 16 + l%16 of the chunk
         // and rows rbase .. rbase+3: the 16x16 MFMA accumulator register i of
         // lane l holds row 4*(l/16) + i (of the wave's 16) for column l%16.
-#pragma unroll
+#pragma unroll 1
         for (int g = 0; g < NG; ++g) {
+            // the newest DBD ancestral deltas of the lane's two beams, in flight
+            // during the projection MFMAs
+            float4 dd[2][DBD];
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int bl = g * 32 + u2 * 16 + n16;
+#pragma unroll
+                for (int u = 0; u < DBD; ++u) {
+                    const int j = depth - 1 - u;
+                    const int r = (bl < nb && j >= 0) ? anc_s[j * CH + bl] : 0;
+                    dd[u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
+                }
+            }
             f32x4 acc[4];                  // tiles: k of beams +0..15, k +16..31, q +0..15, q +16..31
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -390,14 +385,14 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
 #pragma unroll
                         for (int u = 0; u < DBD; ++u)
                             if (jt - u >= 0)
-                                dd[g][u2][u] = *reinterpret_cast<const float4*>(
+                                dd[u2][u] = *reinterpret_cast<const float4*>(
                                     rdelta + anc_s[(jt - u) * CH + bl] * DV + rbase);
                     }
 #pragma unroll
                     for (int u = 0; u < DBD; ++u) {
                         if (jt - u >= 0) {
                             const float4 c = coef_s[(jt - u) * CH + bl];
-                            const float4 dv4 = dd[g][u2][u];
+                            const float4 dv4 = dd[u2][u];
                             const float wk = c.x * sfx, wq = c.y * sfx;
                             sfx *= c.z;
                             zk[0] = fmaf(wk, dv4.x, zk[0]);
