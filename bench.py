@@ -98,6 +98,54 @@ def read_traffic():
         return None
 
 
+def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, command: str) -> str:
+    """Per-launch HBM traffic of the step kernel from two rocprofv3 --pmc runs.
+
+    fetch_dir / write_dir hold run_counter_collection.csv of a run with
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) that also ran one plain device
+    copy of copy_mib MiB. Each counter is scaled by known bytes / counted
+    bytes of that copy. Writes TRAFFIC_FILE and returns its text.
+    """
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0)
+        step = [v for k, (n, v) in sorted(rows.items()) if KERNEL_NAME in n]
+        copy = [v for k, (n, v) in sorted(rows.items()) if "copyBuffer" in n]
+        if not step or not copy:
+            raise SystemExit(f"no {KERNEL_NAME} or copy dispatches with {counter} under {d}")
+        return step, max(copy)
+
+    known = copy_mib * 2.0 ** 20
+    fetch, fetch_copy = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, write_copy = per_kernel(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = known / fetch_copy, known / write_copy
+    per_launch = (sum(fetch) / len(fetch)) * f_scale + (sum(write) / len(write)) * w_scale
+    text = "\n".join([
+        "# HBM traffic of step_kernel on r32_h16_d128_w256_t5 (bytes per launch, all 5 depths averaged)",
+        f"# command: {command}",
+        f"kernel_source_sha = {kernel_source_sha()}",
+        f"copy_probe_bytes = {known:.0f}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"launches = {len(fetch)}",
+        f"fetch_bytes_per_launch = {sum(fetch) / len(fetch) * f_scale:.0f}",
+        f"write_bytes_per_launch = {sum(write) / len(write) * w_scale:.0f}",
+        f"hbm_bytes_per_launch = {per_launch:.0f}",
+        "fetch_bytes_by_dispatch = " + " ".join(f"{x * f_scale:.0f}" for x in fetch),
+        "write_bytes_by_dispatch = " + " ".join(f"{x * w_scale:.0f}" for x in write),
+        "",
+    ])
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    open(TRAFFIC_FILE, "w").write(text)
+    return text
+
+
 # ------------------------------------------------------------ CPU baseline
 def _oracle_pair(args):
     import oracle
@@ -159,11 +207,18 @@ def main():
     ap.add_argument("--steps", type=int, default=50, help="timed episodes")
     ap.add_argument("--warmup", type=int, default=5, help="untimed episodes")
     ap.add_argument("--beams-per-block", type=int, default=0)
-    ap.add_argument("--cpu-pairs", type=int, default=64, help="(request, head) pairs the oracle runs")
+    ap.add_argument("--cpu-pairs", type=int, default=256, help="(request, head) pairs the oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (reference for hardware traffic counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic file and exit")
+    ap.add_argument("--traffic-command", default="", help="command recorded in the traffic file")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.copy_probe or 256,
+                                    args.traffic_command))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requests and heads would shard across GPUs with no exchange inside a step).", file=sys.stderr)
