@@ -71,7 +71,9 @@ typedef int32_t onela_status;
 #define ONELA_E_UNSUPPORTED   (-7)  /* head dims or step count this build has no kernel for */
 
 /* Fixed shape of one context (one GDN layer). Supported: d_k == d_v in
- * {32, 64, 128}; 1 <= beam_width; 1 <= max_steps <= ONELA_MAX_STEPS. */
+ * {32, 64, 128}; 1 <= beam_width; 1 <= max_steps <= ONELA_MAX_STEPS;
+ * beam_width * num_heads * d and max_steps * beam_width * d below 2^31
+ * (otherwise ONELA_E_UNSUPPORTED). */
 #define ONELA_MAX_STEPS 64
 
 typedef struct onela_config {

@@ -96,6 +96,12 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
         return ONELA_E_INVALID_ARG;
     if (!onela::step_supported(cfg->d_k, cfg->d_v) || cfg->max_steps > ONELA_MAX_STEPS)
         return ONELA_E_UNSUPPORTED;
+    // The kernels address one request's inputs and one (request, head)'s
+    // records with 32-bit element offsets.
+    const int64_t dmax = std::max(cfg->d_k, cfg->d_v);
+    if ((int64_t)cfg->beam_width * cfg->num_heads * dmax >= INT32_MAX ||
+        (int64_t)cfg->max_steps * cfg->beam_width * dmax >= INT32_MAX)
+        return ONELA_E_UNSUPPORTED;
 
     onela_ctx* ctx = new onela_ctx();
     ctx->cfg = *cfg;

@@ -38,8 +38,10 @@ def test_create_rejects_bad_configs():
     lib = load_library()
     out = ctypes.c_void_p()
     bad = [(0, 1, 32, 32, 8, 3), (1, 1, 48, 48, 8, 3), (1, 1, 32, 64, 8, 3), (1, 1, 32, 32, 0, 3),
-           (1, 1, 32, 32, 8, 0), (1, 1, 32, 32, 8, 65)]
-    expect = [-1, -7, -7, -1, -1, -7]
+           (1, 1, 32, 32, 8, 0), (1, 1, 32, 32, 8, 65),
+           (1, 64, 32, 32, 1 << 20, 3),      # W*H*d reaches 2^31: 32-bit offsets would overflow
+           (1, 1, 128, 128, 1 << 18, 64)]    # T*W*d reaches 2^31
+    expect = [-1, -7, -7, -1, -1, -7, -7, -7]
     for cfg, e in zip(bad, expect):
         c = _Config(*cfg)
         assert lib.onela_create(ctypes.byref(c), None, ctypes.byref(out)) == e, cfg
