@@ -90,8 +90,9 @@ typedef struct onela_ctx onela_ctx;
 /* Create a context on the current HIP device. hip_stream is a hipStream_t
  * (NULL = the null stream). Allocates S0 planes (4*H*d_v*d_k bytes per
  * request), the record store ((4 + 4*d_v + 2*d_k) bytes per record,
- * max_requests*H*max_steps*W records) and the ancestry index
- * (2*max_requests*W*max_steps int32). On failure *out is NULL. */
+ * max_requests*H*max_steps*W records), the ancestry index
+ * (2*max_requests*W*max_steps int32) and the per-request beam processing
+ * order (2*max_requests*W int32). On failure *out is NULL. */
 onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out);
 
 /* Synchronise the stream and free everything the context owns. NULL is OK. */

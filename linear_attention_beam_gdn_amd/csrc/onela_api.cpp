@@ -21,6 +21,7 @@ struct onela_ctx {
     float* rec_delta = nullptr;
     uint16_t* rec_k = nullptr;
     int32_t* anc = nullptr;
+    int32_t* order = nullptr;
     int32_t* err = nullptr;
     std::vector<int32_t> steps;      // steps done per request; -1 = never initialised
     std::vector<char> poisoned;      // a bad parent index was reported
@@ -112,13 +113,14 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
     const uint64_t nrec = R * H * T * W;
     ctx->s0_bytes = R * H * 2 * dv * dk * 2;
     ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
-    ctx->idx_bytes = 2 * R * W * T * 4 + R * 4;
+    ctx->idx_bytes = 2 * R * W * T * 4 + 2 * R * W * 4 + R * 4;
 
     bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
               hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
               hipMalloc(&ctx->rec_delta, nrec * 4 * dv) == hipSuccess &&
               hipMalloc(&ctx->rec_k, nrec * 2 * dk) == hipSuccess &&
               hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess &&
+              hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess &&
               hipMalloc(&ctx->err, R * 4) == hipSuccess;
     if (!ok) {
         (void)hipGetLastError();
@@ -146,6 +148,7 @@ onela_status onela_destroy(onela_ctx* ctx) {
     (void)hipFree(ctx->rec_delta);
     (void)hipFree(ctx->rec_k);
     (void)hipFree(ctx->anc);
+    (void)hipFree(ctx->order);
     (void)hipFree(ctx->err);
     delete ctx;
     return ONELA_OK;
@@ -206,6 +209,7 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
     p.rec_delta = ctx->rec_delta;
     p.rec_k = ctx->rec_k;
     p.anc = ctx->anc;
+    p.order = ctx->order;
     p.err = ctx->err;
     p.H = c.num_heads;
     p.W = c.beam_width;

@@ -11,6 +11,8 @@ namespace onela {
 constexpr int kMaxReqPerLaunch = 64;
 // Beams one workgroup stages at a time (one chunk of the beam loop).
 constexpr int kChunk = 64;
+// Widest beam set that is processed in ancestry order (the order lives in LDS).
+constexpr int kOrderMax = 1024;
 
 struct StepParams {
     // caller inputs / outputs
@@ -28,6 +30,7 @@ struct StepParams {
     float* rec_delta;           // [max_requests][H][T_max*W][DV]
     uint16_t* rec_k;            // [max_requests][H][T_max*W][DK]
     int32_t* anc;               // [2][max_requests][W][T_max] (ping-pong by step parity)
+    int32_t* order;             // [2][max_requests][W] beam processing order (ping-pong by step parity)
     int32_t* err;               // [max_requests]: epoch of the last step that saw a bad parent
     int32_t H, W, T_max, max_requests;
     int32_t beams_per_block;    // multiple of kChunk, or >= W
@@ -42,6 +45,6 @@ struct StepParams {
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
 bool step_supported(int dk, int dv);
-size_t step_lds_bytes(int dk, int dv, int T_max);
+size_t step_lds_bytes(int dk, int dv, int T_max, int W);
 
 }  // namespace onela

@@ -129,6 +129,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     float* kq_s = reinterpret_cast<float*>(anc_s + CH * MS);        // [CH]: k_t . q_t
     float* at_s = kq_s + CH;                                        // [CH]: alpha_t
     float* bt_s = at_s + CH;                                        // [CH]: beta_t
+    int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [W] processing order (W <= kOrderMax)
+    int* key_s = ord_s + p.W;                                       // [W] sort keys / scratch
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -171,6 +173,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     uint16_t* rkey = p.rec_k + rec0 * DK;                          // record r: rkey + r*DK
     const int* anc_prev = p.anc + ((size_t)((t - 1) & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* anc_next = p.anc + ((size_t)(t & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
+    const int* ord_prev = p.order + ((size_t)((t - 1) & 1) * p.max_requests + slot) * W;
+    int* ord_next = p.order + ((size_t)(t & 1) * p.max_requests + slot) * W;
 
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
     bf16x8 a_hi[KS], a_lo[KS];
@@ -183,6 +187,52 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         }
     }
 
+    // Beams are processed in an order that groups the beam tree: at step t a
+    // beam's sort key is its parent's position in step t-1's order (ties by
+    // beam index), so siblings are adjacent and beams sharing older ancestors
+    // are near each other; a chunk then gathers mostly records that no other
+    // chunk needs. The order only decides which beams share a chunk; each
+    // beam's arithmetic is independent of it. Every workgroup of a request
+    // derives the same order (a deterministic rank), and one writes it for
+    // the next step. Wider beam sets than kOrderMax keep the natural order.
+    const bool ordered = W <= kOrderMax;
+    if (ordered) {
+        if (depth == 0) {
+            for (int i = tid; i < W; i += NT) ord_s[i] = i;
+        } else {
+            for (int i = tid; i < W; i += NT) key_s[min((unsigned)ord_prev[i], (unsigned)(W - 1))] = i;   // position of each step t-1 beam
+            lds_barrier();
+            int ck[(kOrderMax + NT - 1) / NT];
+#pragma unroll
+            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u) {
+                const int b = tid + u * NT;
+                ck[u] = 0;
+                if (b < W) {
+                    const int pb = parin[b];
+                    ck[u] = key_s[(pb < 0 || pb >= W) ? 0 : pb] * W + b;   // unique composite key
+                }
+            }
+            lds_barrier();
+#pragma unroll
+            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u)
+                if (tid + u * NT < W) key_s[tid + u * NT] = ck[u];
+            lds_barrier();
+#pragma unroll
+            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u) {
+                const int b = tid + u * NT;
+                if (b < W) {
+                    int rank = 0;
+                    for (int i = 0; i < W; ++i) rank += key_s[i] < ck[u];
+                    ord_s[rank] = b;
+                }
+            }
+        }
+        lds_barrier();
+        if (h == 0 && split == 0)
+            for (int i = tid; i < W; i += NT) ord_next[i] = ord_s[i];
+    }
+    auto beam_at = [&](int i) __attribute__((always_inline)) { return ordered ? ord_s[i] : i; };
+
     // The replay is linear in the records, so instead of the sequential
     //   y <- alpha_j y + (k_j . x) delta_j      (j = oldest .. newest)
     // the kernel forms
@@ -190,10 +240,10 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // which makes the gathers of all depths independent: key gathers of
     // several depths are in flight together, and the newest block of delta
     // gathers is in flight during the projection MFMAs.
-    const int n16 = lane & 15;                   // MFMA column within a 16-wide tile
-    const int quad = lane >> 4;                  // which 4 rows of the wave's 16 this lane holds
-    const int rbase = wave * kRowsPerWave + quad * 4;
     // Streaming inputs of a chunk: k_t, q_t, v_t, alpha_t, beta_t, parents.
+    // q, k, v are read once and o is written once, so they carry the
+    // non-temporal hint: the caches keep the records, which later chunks and
+    // later steps read again.
     // (Two workgroups share a CU, 128 registers per lane each; latency is
     // hidden by the other workgroup rather than by prefetching in registers.)
     constexpr int SEG = DK / 8;                          // 16-byte pieces per k/q row
@@ -209,7 +259,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // load, the compiler knows exactly how many loads are younger than the
     // one it waits for, and waits for no more than that.
     const int* parsrc = depth > 0 ? parin : reinterpret_cast<const int*>(ain);   // any valid int source at t = 1
-    auto load_stream = [&](int cs) __attribute__((always_inline)) {
+    auto load_stream = [&](int cs, int tid) __attribute__((always_inline)) {
         const int last = min(CH, b_end - cs) - 1;
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
@@ -217,38 +267,47 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             const int row = idx / SEG, seg = idx % SEG;
             const bool is_k = row < CH;
             const int bl = min(is_k ? row : row - CH, last);
-            xv[it] = *reinterpret_cast<const u32x4*>((is_k ? kin : qin) + (cs + bl) * HK + seg * 8);
+            xv[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>((is_k ? kin : qin) + beam_at(cs + bl) * HK + seg * 8));
         }
 #pragma unroll
         for (int it = 0; it < VITER; ++it) {
             const int idx = tid + it * NT;
             const int bl = min(idx / VSEG, last), seg = idx % VSEG;
-            vv[it] = *reinterpret_cast<const u32x4*>(vin + (cs + bl) * HV + seg * 8);
+            vv[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vin + beam_at(cs + bl) * HV + seg * 8));
         }
         const int bq = min(tid, last);
-        a_new = ain[(cs + bq) * H];
-        b_new = bin[(cs + bq) * H];
-        par = parsrc[cs + bq];
+        const int bb = beam_at(cs + bq);
+        a_new = ain[bb * H];
+        b_new = bin[bb * H];
+        par = parsrc[bb];
     };
 
     for (int c0 = b_begin; c0 < b_end; c0 += CH) {
         const int nb = min(CH, b_end - c0);
+        // Per-lane index values are re-derived every chunk from an opaque copy
+        // of the thread id: cheaper than holding them (and the LDS addresses
+        // made from them) in registers across the loop at 128 per lane.
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
+        const int n16 = tid_l & 15;                  // MFMA column within a 16-wide tile
+        const int quad = (tid_l & 63) >> 4;          // which 4 rows of the wave's 16 this lane holds
+        const int rbase = wave * kRowsPerWave + quad * 4;
 
         // ---- A. stage k_t, q_t, v_t, alpha_t, beta_t; ancestry rows ---------
-        load_stream(c0);
-        const bool beam_thread = tid < nb;                   // one thread per beam of the chunk
+        load_stream(c0, tid_l);
+        const bool beam_thread = tid_l < nb;                   // one thread per beam of the chunk
         if (beam_thread && depth > 0) {
             if (par < 0 || par >= W) {                       // reported through the error word
                 p.err[slot] = p.epoch[ri];
                 par = 0;
             }
             const int* src = anc_prev + par * p.T_max;
-            for (int j = 0; j + 1 < depth; ++j) anc_s[j * CH + tid] = src[j];
-            anc_s[(depth - 1) * CH + tid] = (depth - 1) * W + par;   // parent's own record of step t-1
+            for (int j = 0; j + 1 < depth; ++j) anc_s[j * CH + tid_l] = src[j];
+            anc_s[(depth - 1) * CH + tid_l] = (depth - 1) * W + par;   // parent's own record of step t-1
         }
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
-            const int idx = tid + it * NT;
+            const int idx = tid_l + it * NT;
             if (idx < 2 * CH * SEG) {
                 const int row = idx / SEG, seg = idx % SEG;
                 *reinterpret_cast<u32x4*>(xs + row * XS + seg * 8) = xv[it];
@@ -256,15 +315,15 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         }
 #pragma unroll
         for (int it = 0; it < VITER; ++it) {
-            const int idx = tid + it * NT;
+            const int idx = tid_l + it * NT;
             if (idx < CH * VSEG) {
                 const int bl = idx / VSEG, seg = idx % VSEG;
                 *reinterpret_cast<u32x4*>(vs + bl * VS + seg * 8) = vv[it];
             }
         }
         if (beam_thread) {
-            at_s[tid] = a_new;
-            bt_s[tid] = b_new;
+            at_s[tid_l] = a_new;
+            bt_s[tid_l] = b_new;
         }
         lds_barrier();
 
@@ -326,7 +385,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             consume_units(u0);
         }
         {   // k_t . q_t on the vector units, from LDS
-            const int bl = tid / TPQ, part = tid % TPQ;
+            const int bl = tid_l / TPQ, part = tid_l % TPQ;
             const uint16_t* kt_s = xs + bl * XS + part * EQ;
             const uint16_t* qt_s = xs + (CH + bl) * XS + part * EQ;
             float kq = 0.f;
@@ -408,7 +467,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 }
                 // sfx is now the product of alpha over the whole history
                 const f32x4 yk = acc[u2] * sfx + zk, yq = acc[2 + u2] * sfx + zq;
-                const int b = c0 + bl;
+                const int b = beam_at(c0 + bl);
                 const float kq = kq_s[bl], a = at_s[bl], bb = bt_s[bl];
                 const uint2 vb = *reinterpret_cast<const uint2*>(vs + bl * VS + rbase);
                 float4 d, o;
@@ -420,7 +479,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 o.y = fmaf(a, yq[1], kq * d.y);
                 o.z = fmaf(a, yq[2], kq * d.z);
                 o.w = fmaf(a, yq[3], kq * d.w);
-                *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
+                __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4*>(oout + b * HV + rbase));
                 *reinterpret_cast<float4*>(rdelta + (depth * W + b) * DV + rbase) = d;
                 if (dout) *reinterpret_cast<float4*>(dout + b * HV + rbase) = d;
             }
@@ -429,17 +488,17 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         // ---- append k_t, alpha_t and the new index rows (after every gather) -
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
-            const int idx = tid + it * NT;
+            const int idx = tid_l + it * NT;
             const int row = idx / SEG, seg = idx % SEG;
             if (idx < 2 * CH * SEG && row < nb)
-                *reinterpret_cast<uint4*>(rkey + (depth * W + c0 + row) * DK + seg * 8) =
+                *reinterpret_cast<uint4*>(rkey + (depth * W + beam_at(c0 + row)) * DK + seg * 8) =
                     *reinterpret_cast<const uint4*>(xs + row * XS + seg * 8);
         }
         if (beam_thread) {
-            const int b = c0 + tid;
-            ralpha[depth * W + b] = at_s[tid];              // a_new already holds the next chunk's
+            const int b = beam_at(c0 + tid_l);
+            ralpha[depth * W + b] = at_s[tid_l];
             if (h == 0)   // one head writes the request's new index rows
-                for (int j = 0; j < depth; ++j) anc_next[b * p.T_max + j] = anc_s[j * CH + tid];
+                for (int j = 0; j < depth; ++j) anc_next[b * p.T_max + j] = anc_s[j * CH + tid_l];
         }
         lds_barrier();   // LDS is reused by the next chunk
     }
@@ -454,7 +513,7 @@ hipError_t launch_init_t(const float* S0, uint16_t* planes, int H, hipStream_t s
 
 template <int DK, int DV>
 hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
-    const size_t lds = step_lds_bytes(DK, DV, p.T_max);
+    const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -467,13 +526,14 @@ hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
 
 }  // namespace
 
-size_t step_lds_bytes(int dk, int dv, int T_max) {
+size_t step_lds_bytes(int dk, int dv, int T_max, int W) {
     const size_t ms = T_max > 1 ? (size_t)T_max - 1 : 1;
     return kChunk * ms * 16                       // coef_s
            + 2 * kChunk * (size_t)(dk + 8) * 2    // xs
            + kChunk * (size_t)(dv + 8) * 2        // vs
            + kChunk * ms * 4                      // anc_s
-           + 3 * kChunk * 4;                      // kq_s, at_s, bt_s
+           + 3 * kChunk * 4                       // kq_s, at_s, bt_s
+           + (W <= kOrderMax ? 2 * (size_t)W * 4 : 0);   // ord_s, key_s
 }
 
 bool step_supported(int dk, int dv) {
