@@ -241,9 +241,10 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // several depths are in flight together, and the newest block of delta
     // gathers is in flight during the projection MFMAs.
     // Streaming inputs of a chunk: k_t, q_t, v_t, alpha_t, beta_t, parents.
-    // q, k, v are read once and o is written once, so they carry the
-    // non-temporal hint: the caches keep the records, which later chunks and
-    // later steps read again.
+    // q, k, v are read once, so they carry the non-temporal hint: the caches
+    // keep the records, which later chunks and later steps read again. (o is
+    // written in 64-byte pieces by several waves and stays a normal store, so
+    // the L2 merges the pieces into whole lines.)
     // (Two workgroups share a CU, 128 registers per lane each; latency is
     // hidden by the other workgroup rather than by prefetching in registers.)
     constexpr int SEG = DK / 8;                          // 16-byte pieces per k/q row
@@ -479,13 +480,13 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 o.y = fmaf(a, yq[1], kq * d.y);
                 o.z = fmaf(a, yq[2], kq * d.z);
                 o.w = fmaf(a, yq[3], kq * d.w);
-                __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<f32x4*>(oout + b * HV + rbase));
+                *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
                 *reinterpret_cast<float4*>(rdelta + (depth * W + b) * DV + rbase) = d;
                 if (dout) *reinterpret_cast<float4*>(dout + b * HV + rbase) = d;
             }
         }
 
-        // ---- append k_t, alpha_t and the new index rows (after every gather) -
+        // ---- append k_t (whole 256-byte rows) after every gather ------------
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
             const int idx = tid_l + it * NT;
@@ -494,13 +495,20 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 *reinterpret_cast<uint4*>(rkey + (depth * W + beam_at(c0 + row)) * DK + seg * 8) =
                     *reinterpret_cast<const uint4*>(xs + row * XS + seg * 8);
         }
-        if (beam_thread) {
-            const int b = beam_at(c0 + tid_l);
-            ralpha[depth * W + b] = at_s[tid_l];
-            if (h == 0)   // one head writes the request's new index rows
-                for (int j = 0; j < depth; ++j) anc_next[b * p.T_max + j] = anc_s[j * CH + tid_l];
-        }
         lds_barrier();   // LDS is reused by the next chunk
+    }
+
+    // ---- alpha_t records and the request's new index rows, in beam-index
+    // order over this workgroup's index range (the splits of a (request,
+    // head) cover [0, W) between them), so the small writes coalesce.
+    for (int b = b_begin + tid; b < b_end; b += NT) {
+        ralpha[depth * W + b] = ain[b * H];
+        if (h == 0 && depth > 0) {                     // one head writes the index
+            int pb = parin[b];
+            pb = (pb < 0 || pb >= W) ? 0 : pb;         // (reported in phase A)
+            for (int j = 0; j + 1 < depth; ++j) anc_next[b * p.T_max + j] = anc_prev[pb * p.T_max + j];
+            anc_next[b * p.T_max + depth - 1] = (depth - 1) * W + pb;
+        }
     }
 }
 
