@@ -146,6 +146,52 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, command
     return text
 
 
+def fullstate_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela_ms_per_step, onela_mem):
+    """Same workload through the full-state comparator (a full state per beam)."""
+    import torch
+
+    from linear_attention_beam_gdn_amd import FullState
+
+    R, H, W, T = shape.R, shape.H, shape.W, shape.T
+    fs = FullState(R, H, shape.dk, shape.dv, W, T, stream=stream)
+    for r in range(R):
+        fs.init_request(r, S0[r].contiguous())
+    reqs = list(range(R))
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+    per_t, walls = [], []
+    for it in range(4):
+        for r in reqs:
+            fs.reset(r)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(T):
+            ev[t][0].record(stream)
+            fs.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t], o)
+            ev[t][1].record(stream)
+        torch.cuda.synchronize()
+        if it:
+            walls.append(time.perf_counter() - t0)
+            per_t.append([ev[t][0].elapsed_time(ev[t][1]) for t in range(T)])
+    fs.sync()
+    fs_mem = fs.memory()
+    fs.close()
+    sz = shape.dv * shape.dk * 4
+    fs_launch_s = float(np.mean(per_t)) * 1e-3
+    onela_persistent = onela_mem["s0_bytes"] + onela_mem["record_bytes"] + onela_mem["index_bytes"]
+    per_beam_states = R * H * W * sz
+    return {
+        "what": "the same decode steps with a full d_v x d_k float32 state per beam (gather the parent's, write the new)",
+        "kernel_us_mean": fs_launch_s * 1e6,
+        "us_per_decode_step": float(np.median(walls)) / T * 1e6,
+        "us_per_decode_step_by_depth": [round(float(x) * 1e3, 1) for x in np.median(np.array(per_t), axis=0)],
+        "speedup_kernel": fs_launch_s / onela_launch_s,
+        "speedup_step": float(np.median(walls)) / T * 1e3 / (onela_ms_per_step / T),
+        "persistent_state_bytes": {"onela": onela_persistent, "fullstate_per_beam_states": per_beam_states,
+                                   "fullstate_allocated": fs_mem},
+        "state_reduction": per_beam_states / onela_persistent,
+    }
+
+
 # ------------------------------------------------------------ CPU baseline
 def _oracle_pair(args):
     import oracle
@@ -209,6 +255,7 @@ def main():
     ap.add_argument("--beams-per-block", type=int, default=0)
     ap.add_argument("--cpu-pairs", type=int, default=256, help="(request, head) pairs the oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fullstate", action="store_true", help="skip the full-state comparator leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (reference for hardware traffic counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -342,9 +389,13 @@ def main():
         },
         "input_generation_s": round(t_gen, 1),
     }
+    mem = lay.memory()
+    lay.close()
+    if not args.no_fullstate:
+        out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o, up(ep["S0"]), stream,
+                                                    mean_launch_s, ms_per_step, mem)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)
-    lay.close()
     print(json.dumps(out), flush=True)
 
 

@@ -160,6 +160,33 @@ onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_
 onela_status onela_get_memory(const onela_ctx* ctx, uint64_t* s0_bytes,
                               uint64_t* record_bytes, uint64_t* index_bytes);
 
+/* ---- comparator: a full state per beam ---------------------------------
+ * The decode step OneLA replaces (OneLA review, evolve.pub, "Summary" and
+ * "Scope & Claims": the FullState serving path keeps a full d_v x d_k state
+ * for every beam, Theta(W d_v d_k) memory and traffic per step). Same
+ * recurrence, conventions, argument layouts and error behaviour as the
+ * onela_* calls above; the library owns S0 copies and two float32 states per
+ * (request, head, beam) (the parents' and the new ones), allocated in
+ * onela_fs_create. Used to measure what the shared-state representation saves.
+ */
+typedef struct onela_fs_ctx onela_fs_ctx;
+
+/* Allocates 4*d_v*d_k*max_requests*num_heads*(2*beam_width + 1) bytes. */
+onela_status onela_fs_create(const onela_config* cfg, void* hip_stream, onela_fs_ctx** out);
+onela_status onela_fs_destroy(onela_fs_ctx* ctx);
+/* Copies S0 (device float32 [H][d_v][d_k]) and rewinds the request to step 0. */
+onela_status onela_fs_init_request(onela_fs_ctx* ctx, int32_t req, const float* S0);
+/* One decode step; arguments as for onela_step. Reads each beam's parent
+ * state, writes the beam's new state, o and optionally delta. */
+onela_status onela_fs_step(onela_fs_ctx* ctx, int32_t n_req, const int32_t* reqs,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* alpha, const float* beta,
+                           const int32_t* parent_idx, float* o, float* delta_out);
+onela_status onela_fs_reset(onela_fs_ctx* ctx, int32_t req);
+onela_status onela_fs_sync(onela_fs_ctx* ctx);
+/* Device bytes of persistent state the comparator owns. */
+onela_status onela_fs_get_memory(const onela_fs_ctx* ctx, uint64_t* state_bytes);
+
 /* Static text for a status code. */
 const char* onela_status_string(onela_status s);
 

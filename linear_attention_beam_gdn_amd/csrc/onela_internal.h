@@ -41,7 +41,28 @@ struct StepParams {
     int32_t epoch[kMaxReqPerLaunch]; // its episode number (> 0), written to err on a bad parent
 };
 
+// The full-state comparator (every beam keeps its own d_v x d_k state).
+struct FullStateParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* alpha;
+    const float* beta;
+    const int32_t* parent;
+    float* o;
+    float* delta_out;
+    const float* s0;            // [max_requests][H][DV*DK] float32
+    float* state;               // [2][max_requests][H][W][DV*DK] float32 (ping-pong by step parity)
+    int32_t* err;               // [max_requests]
+    int32_t H, W, max_requests;
+    int32_t n_req;
+    int32_t slot[kMaxReqPerLaunch];
+    int32_t t[kMaxReqPerLaunch];
+    int32_t epoch[kMaxReqPerLaunch];
+};
+
 // Returns hipErrorInvalidValue for unsupported (DK, DV).
+hipError_t launch_fullstate_step(int dk, int dv, const FullStateParams& p, hipStream_t s);
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
 bool step_supported(int dk, int dv);

@@ -29,6 +29,8 @@ EXPORTED = (
     "onela_create", "onela_destroy", "onela_init_request", "onela_step", "onela_reset",
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
+    "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
+    "onela_fs_sync", "onela_fs_get_memory",
 )
 
 
@@ -69,6 +71,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_get_records": (i32, [vp, i32, i32, i32, vp, vp, vp]),
         "onela_get_memory": (i32, [vp, vp, vp, vp]),
         "onela_status_string": (ctypes.c_char_p, [i32]),
+        "onela_fs_create": (i32, [ctypes.POINTER(_Config), vp, ctypes.POINTER(vp)]),
+        "onela_fs_destroy": (i32, [vp]),
+        "onela_fs_init_request": (i32, [vp, i32, vp]),
+        "onela_fs_step": (i32, [vp, i32, p_i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "onela_fs_reset": (i32, [vp, i32]),
+        "onela_fs_sync": (i32, [vp]),
+        "onela_fs_get_memory": (i32, [vp, vp]),
         "onela_last_error": (ctypes.c_char_p, [vp]),
     }
     for name, (res, args) in sigs.items():
@@ -199,3 +208,72 @@ class Onela:
         self._check(self.lib.onela_get_memory(self._ctx, ctypes.byref(s0), ctypes.byref(rec), ctypes.byref(idx)),
                     "onela_get_memory")
         return {"s0_bytes": s0.value, "record_bytes": rec.value, "index_bytes": idx.value}
+
+
+class FullState:
+    """The comparator that keeps a full d_v x d_k state per beam (same calls as Onela)."""
+
+    def __init__(self, max_requests, num_heads, d_k, d_v, beam_width, max_steps, stream=None):
+        import torch
+
+        self._torch = torch
+        self.lib = load_library()
+        self.cfg = _Config(max_requests, num_heads, d_k, d_v, beam_width, max_steps)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._ctx = ctypes.c_void_p()
+        st = self.lib.onela_fs_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.stream.cuda_stream),
+                                      ctypes.byref(self._ctx))
+        if st != ONELA_OK:
+            raise OnelaError(st, "onela_fs_create")
+
+    def _check(self, status, where):
+        if status != ONELA_OK:
+            raise OnelaError(status, where)
+
+    def close(self):
+        if self._ctx:
+            self.lib.onela_fs_destroy(self._ctx)
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def init_request(self, req: int, S0):
+        c = self.cfg
+        p = _ptr(S0, "S0", (self._torch.float32,), (c.num_heads, c.d_v, c.d_k))
+        self._check(self.lib.onela_fs_init_request(self._ctx, req, p), "onela_fs_init_request")
+
+    def step(self, reqs, q, k, v, alpha, beta, parent_idx, o, delta_out=None):
+        torch = self._torch
+        c = self.cfg
+        n = len(reqs)
+        rows = n * c.beam_width
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        f32 = (torch.float32,)
+        arr = (ctypes.c_int32 * n)(*[int(r) for r in reqs])
+        st = self.lib.onela_fs_step(
+            self._ctx, n, arr,
+            _ptr(q, "q", bf, (rows, c.num_heads, c.d_k)),
+            _ptr(k, "k", bf, (rows, c.num_heads, c.d_k)),
+            _ptr(v, "v", bf, (rows, c.num_heads, c.d_v)),
+            _ptr(alpha, "alpha", f32, (rows, c.num_heads)),
+            _ptr(beta, "beta", f32, (rows, c.num_heads)),
+            _ptr(parent_idx, "parent_idx", (torch.int32,), (n, c.beam_width), optional=True),
+            _ptr(o, "o", f32, (rows, c.num_heads, c.d_v)),
+            _ptr(delta_out, "delta_out", f32, (rows, c.num_heads, c.d_v), optional=True),
+        )
+        self._check(st, "onela_fs_step")
+
+    def reset(self, req: int):
+        self._check(self.lib.onela_fs_reset(self._ctx, req), "onela_fs_reset")
+
+    def sync(self):
+        self._check(self.lib.onela_fs_sync(self._ctx), "onela_fs_sync")
+
+    def memory(self) -> int:
+        b = ctypes.c_uint64()
+        self._check(self.lib.onela_fs_get_memory(self._ctx, ctypes.byref(b)), "onela_fs_get_memory")
+        return b.value
