@@ -115,7 +115,7 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, command
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
                     rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0)
-        step = [v for k, (n, v) in sorted(rows.items()) if KERNEL_NAME in n]
+        step = [v for k, (n, v) in sorted(rows.items()) if f"::{KERNEL_NAME}<" in n]   # not fs_step_kernel
         copy = [v for k, (n, v) in sorted(rows.items()) if "copyBuffer" in n]
         if not step or not copy:
             raise SystemExit(f"no {KERNEL_NAME} or copy dispatches with {counter} under {d}")

@@ -129,8 +129,11 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     float* kq_s = reinterpret_cast<float*>(anc_s + CH * MS);        // [CH]: k_t . q_t
     float* at_s = kq_s + CH;                                        // [CH]: alpha_t
     float* bt_s = at_s + CH;                                        // [CH]: beta_t
-    int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [W] processing order (W <= kOrderMax)
-    int* key_s = ord_s + p.W;                                       // [W] sort keys / scratch
+    const int Wp = (p.W + 3) & ~3;                                   // W rounded up to whole int4s
+    int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] processing order (W <= kOrderMax)
+    int* pos_s = reinterpret_cast<int*>(xs);                        // [Wp] before the beam loop: step t-1 positions
+    int* ck_s = pos_s + Wp;                                         // [Wp] before the beam loop: sort keys
+    static_assert(2 * CH * XS * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q staging area");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,6 +179,22 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     const int* ord_prev = p.order + ((size_t)((t - 1) & 1) * p.max_requests + slot) * W;
     int* ord_next = p.order + ((size_t)(t & 1) * p.max_requests + slot) * W;
 
+    // The previous order and this step's parents are loaded before S0, so
+    // the ordering below runs while the S0 fragments are in flight (indices
+    // clamped into the arrays; at t = 1 there is no parent to order by).
+    const bool ordered = W <= kOrderMax;
+    constexpr int OU = (kOrderMax + NT - 1) / NT;
+    int po[OU] = {}, pa[OU] = {};
+    if (depth > 0) {
+#pragma unroll
+        for (int u = 0; u < OU; ++u) {
+            const int i = min(tid + u * NT, W - 1);
+            po[u] = ord_prev[i];
+            pa[u] = parin[i];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
     bf16x8 a_hi[KS], a_lo[KS];
     {
@@ -195,36 +214,42 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // beam's arithmetic is independent of it. Every workgroup of a request
     // derives the same order (a deterministic rank), and one writes it for
     // the next step. Wider beam sets than kOrderMax keep the natural order.
-    const bool ordered = W <= kOrderMax;
     if (ordered) {
         if (depth == 0) {
             for (int i = tid; i < W; i += NT) ord_s[i] = i;
         } else {
-            for (int i = tid; i < W; i += NT) key_s[min((unsigned)ord_prev[i], (unsigned)(W - 1))] = i;   // position of each step t-1 beam
-            lds_barrier();
-            int ck[(kOrderMax + NT - 1) / NT];
 #pragma unroll
-            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u) {
-                const int b = tid + u * NT;
-                ck[u] = 0;
-                if (b < W) {
-                    const int pb = parin[b];
-                    ck[u] = key_s[(pb < 0 || pb >= W) ? 0 : pb] * W + b;   // unique composite key
-                }
+            for (int u = 0; u < OU; ++u) {
+                const int i = tid + u * NT;
+                if (i < W) pos_s[min((unsigned)po[u], (unsigned)(W - 1))] = i;   // position of each step t-1 beam
             }
             lds_barrier();
 #pragma unroll
-            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u)
-                if (tid + u * NT < W) key_s[tid + u * NT] = ck[u];
+            for (int u = 0; u < OU; ++u) {
+                const int i = tid + u * NT;
+                const int pb = pa[u];
+                if (i < Wp)   // unique composite keys; the padding sorts last
+                    ck_s[i] = i < W ? pos_s[(pb < 0 || pb >= W) ? 0 : pb] * W + i : 0x7fffffff;
+            }
             lds_barrier();
-#pragma unroll
-            for (int u = 0; u < (kOrderMax + NT - 1) / NT; ++u) {
-                const int b = tid + u * NT;
-                if (b < W) {
-                    int rank = 0;
-                    for (int i = 0; i < W; ++i) rank += key_s[i] < ck[u];
-                    ord_s[rank] = b;
+            // rank of each key among all keys: G adjacent lanes share a beam
+            // and split its key range, reading four keys per LDS access
+            int G = 1;
+            while (G < 8 && 2 * G * W <= NT) G <<= 1;
+            const int g = tid & (G - 1);
+            const int nq = Wp >> 2;
+            const int4* ck4 = reinterpret_cast<const int4*>(ck_s);
+            for (int b0 = 0; b0 < W; b0 += NT / G) {
+                const int b = b0 + tid / G;
+                const int c = ck_s[min(b, W - 1)];
+                int r = 0;
+#pragma unroll 4
+                for (int qd = g; qd < nq; qd += G) {
+                    const int4 kv = ck4[qd];
+                    r += (kv.x < c) + (kv.y < c) + (kv.z < c) + (kv.w < c);
                 }
+                for (int m = 1; m < G; m <<= 1) r += __shfl_xor(r, m, 64);
+                if (g == 0 && b < W) ord_s[r] = b;
             }
         }
         lds_barrier();
@@ -541,7 +566,7 @@ size_t step_lds_bytes(int dk, int dv, int T_max, int W) {
            + kChunk * (size_t)(dv + 8) * 2        // vs
            + kChunk * ms * 4                      // anc_s
            + 3 * kChunk * 4                       // kq_s, at_s, bt_s
-           + (W <= kOrderMax ? 2 * (size_t)W * 4 : 0);   // ord_s, key_s
+           + (W <= kOrderMax ? (size_t)((W + 3) & ~3) * 4 : 0);   // ord_s
 }
 
 bool step_supported(int dk, int dv) {
