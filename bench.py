@@ -1,8 +1,11 @@
 """Throughput of the OneLA GDN beam decode step on one MI355X.
 
 Workload: 32 concurrent requests x 16 heads, d_k = d_v = 128, beam width 256,
-5 decode steps per episode, S0 ~ N(0, 0.05^2) per head, parents chosen per
-request as the top W of 4W beam-search-like candidates. One bench step is one
+5 decode steps per episode, parents chosen per request as the top W of 4W
+beam-search-like candidates. S0 is prompt-derived: a 5120-token synthetic
+prompt per request is folded on the GPU by the prefill kernel (--s0 normal
+draws S0 ~ N(0, 0.05^2) instead; the decode step's cost does not depend on
+S0's values). One bench step is one
 episode: every request is rewound (host-only) and advanced through all 5
 decode steps of one GDN layer, one library launch per decode step. All inputs
 of the 5 steps are resident in HBM before timing starts.
@@ -32,6 +35,7 @@ from workload import bf16_bits_to_f32, make_episode, shape_of  # noqa: E402
 METRIC = "GDN beam-steps/sec + µs/decode-step at W=256,d_k=d_v=128; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 KERNEL_NAME = "step_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_r32_h16_w256_t5_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_beam_gdn_amd", "csrc", "onela_kernels.hip")
@@ -146,6 +150,46 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, command
     return text
 
 
+def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
+    """Fold a synthetic prompt per request into the layer's S0 on the GPU and time it.
+
+    Returns (float32 S0 [R][H][dv][dk] for the comparator or None, prefill record).
+    The prefill is ALU-bound: per token and head it does d_v d_k multiply-adds
+    for S k and d_v d_k multiplies plus multiply-adds for the update, counted
+    as 5 d_v d_k flops.
+    """
+    import torch
+
+    from linear_attention_beam_gdn_amd import prefill
+    from workload.gen_device import prompt_tokens_device
+
+    pshape = shape_of(shape.cfg, s0="prompt", prompt_len=prompt_len)
+    toks = prompt_tokens_device(pshape, dev, reqs=reqs)
+    args = (toks["k"], toks["v"], toks["alpha"], toks["beta"])
+    lay.init_requests_from_prompts(reqs, *args)       # warm-up (and the state the bench decodes from)
+    ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+    ev[0].record(stream)
+    lay.init_requests_from_prompts(reqs, *args)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    S0 = prefill(*args, stream=stream) if need_f32 else None
+    torch.cuda.synchronize()
+    del toks, args
+    flops = 5.0 * len(reqs) * prompt_len * shape.H * shape.dv * shape.dk
+    tflops = flops / (ms * 1e-3) / 1e12
+    return S0, {
+        "kernel": "prefill_kernel",
+        "what": f"S0 of {len(reqs)} requests x {shape.H} heads from {prompt_len}-token prompts, one launch "
+                "(onela_init_requests_from_prompts, written as the step kernel's bf16 planes)",
+        "ms": ms,
+        "tokens_per_s": len(reqs) * prompt_len / (ms * 1e-3),
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "flops_per_launch": flops},
+    }
+
+
 def fullstate_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela_ms_per_step, onela_mem):
     """Same workload through the full-state comparator (a full state per beam)."""
     import torch
@@ -230,8 +274,8 @@ def cpu_baseline(shape, ep, n_pairs: int):
         "cores": min(cores, n_pairs),
         "kind": "oracle",
         "sample": (f"{n_pairs} (request, head) pairs of {shape.name}, all {shape.T} steps, float64 full state "
-                   f"per beam; {wall:.1f} s wall, {sum(per_pair):.1f} s CPU; scaled by {shape.H} heads per "
-                   "beam-step"),
+                   f"per beam, from a drawn S0 (the oracle's cost does not depend on S0's values); "
+                   f"{wall:.1f} s wall, {sum(per_pair):.1f} s CPU; scaled by {shape.H} heads per beam-step"),
         "cpu_model": _cpu_model(),
     }
 
@@ -256,6 +300,9 @@ def main():
     ap.add_argument("--cpu-pairs", type=int, default=256, help="(request, head) pairs the oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fullstate", action="store_true", help="skip the full-state comparator leg")
+    ap.add_argument("--s0", choices=("prompt", "normal"), default="prompt",
+                    help="S0 folded on the GPU from a synthetic prompt (default) or drawn N(0, 0.05^2)")
+    ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (reference for hardware traffic counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -305,9 +352,18 @@ def main():
     lay = Onela(R, H, dk, dv, W, T, stream=stream)
     if args.beams_per_block:
         lay.set_beams_per_block(args.beams_per_block)
-    for r in range(R):
-        lay.init_request(r, up(ep["S0"][r]))
     reqs = list(range(R))
+    prefill_out = None
+    if args.s0 == "prompt":
+        S0_dev, prefill_out = prompt_s0(lay, shape, args.prompt_len, reqs, dev, stream,
+                                        need_f32=not args.no_fullstate)
+        s0_label = (f"prompt-derived: the GDN recurrence over {args.prompt_len} synthetic tokens per request "
+                    "and head, folded on the GPU (prefill_kernel)")
+    else:
+        for r in range(R):
+            lay.init_request(r, up(ep["S0"][r]))
+        S0_dev = None
+        s0_label = "N(0, 0.05^2) float32 per head"
 
     def episode(events=None):
         for r in reqs:
@@ -362,7 +418,7 @@ def main():
         "config": {
             "workload": shape.name,
             "requests": R, "heads": H, "d_k": dk, "d_v": dv, "beam_width": W, "decode_steps": T,
-            "s0": "N(0, 0.05^2) float32 per head", "parents": "top W of 4W candidates per request",
+            "s0": s0_label, "parents": "top W of 4W candidates per request",
             "inputs": "bf16 q, k (L2-normalised), v; float32 alpha, beta",
             "step": "one episode = host rewind + 5 decode steps of one GDN layer, one launch each",
         },
@@ -389,10 +445,13 @@ def main():
         },
         "input_generation_s": round(t_gen, 1),
     }
+    if prefill_out is not None:
+        out["prefill"] = prefill_out
     mem = lay.memory()
     lay.close()
     if not args.no_fullstate:
-        out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o, up(ep["S0"]), stream,
+        out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o,
+                                                    up(ep["S0"]) if S0_dev is None else S0_dev, stream,
                                                     mean_launch_s, ms_per_step, mem)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)

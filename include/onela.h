@@ -106,6 +106,35 @@ onela_status onela_destroy(onela_ctx* ctx);
  * call. */
 onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0);
 
+/* Like onela_init_request for n_req requests at once, with each S0 computed
+ * on the GPU from the request's prompt: the GDN recurrence (OneLA review,
+ * evolve.pub, paper Eq. 2) run over seq_len tokens from a zero state and
+ * written straight into the library's two bf16 planes (OneLA abstract: the
+ * shared state is prompt-derived). reqs: host [n_req], distinct ids.
+ * k: device bf16 [n_req][seq_len][H][d_k]; v: device bf16
+ * [n_req][seq_len][H][d_v]; alpha, beta: device float32 [n_req][seq_len][H];
+ * k and v 16-byte aligned. seq_len = 0 gives the zero state. Same state
+ * change as onela_init_request for every listed request (step 0, poison
+ * cleared); one workgroup per (request, head). */
+onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
+                                              int32_t seq_len, const uint16_t* k, const uint16_t* v,
+                                              const float* alpha, const float* beta);
+
+/* Prefill without a context: fold n_seq prompts of seq_len tokens each into
+ * float32 states with the GDN recurrence (OneLA review, evolve.pub, paper
+ * Eq. 2), per sequence and head, starting from S_init (device float32
+ * [n_seq][H][d_v][d_k], or NULL for the zero state). Layouts: k device bf16
+ * [n_seq][seq_len][H][d_k]; v [n_seq][seq_len][H][d_v]; alpha, beta float32
+ * [n_seq][seq_len][H]; S_out device float32 [n_seq][H][d_v][d_k]. S_out may
+ * equal S_init (in place). Folding a prompt in two calls (the second starting
+ * from the first's S_out) gives bit-identical states to one call. Pointers of
+ * k, v, S_init, S_out are 16-byte aligned; d_k = d_v in {32, 64, 128}
+ * (else ONELA_E_UNSUPPORTED). Asynchronous on hip_stream (NULL = the null
+ * stream); errors of the launch itself return ONELA_E_HIP. Allocates nothing. */
+onela_status onela_prefill(int32_t n_seq, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t seq_len,
+                           const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+                           const float* S_init, float* S_out, void* hip_stream);
+
 /* One decode step of one GDN layer for n_req requests (OneLA review,
  * "Key claims" and "Scope & Claims", paper Eq. 2-4: records (alpha, delta, k)
  * appended per step, projection replay over the ancestry).

@@ -28,7 +28,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["onela_kernels.hip", "onela_api.cpp", "fullstate_kernels.hip", "fullstate_api.cpp"]
+SOURCES = ["onela_kernels.hip", "onela_api.cpp", "fullstate_kernels.hip", "fullstate_api.cpp",
+           "prefill_kernels.hip", "prefill_api.cpp"]
 
 
 def hipcc() -> str:

@@ -166,6 +166,45 @@ onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0) {
     return ONELA_OK;
 }
 
+onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, int32_t seq_len,
+                                              const uint16_t* k, const uint16_t* v, const float* alpha,
+                                              const float* beta) {
+    if (!ctx || n_req < 1 || !reqs || seq_len < 0) return ONELA_E_INVALID_ARG;
+    if (seq_len > 0 && (!k || !v || !alpha || !beta)) return ONELA_E_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 4) || !aligned(beta, 4)) return ONELA_E_INVALID_ARG;
+    const auto& c = ctx->cfg;
+    std::vector<char> seen(c.max_requests, 0);
+    for (int i = 0; i < n_req; ++i) {
+        if (!valid_req(ctx, reqs[i]) || seen[reqs[i]]) return ONELA_E_INVALID_ARG;
+        seen[reqs[i]] = 1;
+    }
+    const size_t tok = (size_t)seq_len * c.num_heads;                 // rows of one request's prompt
+    for (int i0 = 0; i0 < n_req; i0 += onela::kMaxReqPerLaunch) {
+        const int n = std::min(onela::kMaxReqPerLaunch, n_req - i0);
+        onela::PrefillParams p{};
+        p.k = k ? k + i0 * tok * c.d_k : nullptr;
+        p.v = v ? v + i0 * tok * c.d_v : nullptr;
+        p.alpha = alpha ? alpha + i0 * tok : nullptr;
+        p.beta = beta ? beta + i0 * tok : nullptr;
+        p.s_init = nullptr;
+        p.s_out = nullptr;
+        p.planes = ctx->s0_planes;
+        p.n_seq = n;
+        p.H = c.num_heads;
+        p.L = seq_len;
+        for (int i = 0; i < n; ++i) p.slot[i] = reqs[i0 + i];
+        hipError_t e = onela::launch_prefill(c.d_k, c.d_v, true, p, ctx->stream);
+        if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
+    }
+    for (int i = 0; i < n_req; ++i) {
+        const int r = reqs[i];
+        ctx->steps[r] = 0;
+        ctx->poisoned[r] = 0;
+        ctx->epoch[r] = ctx->epoch[r] == INT32_MAX ? 1 : ctx->epoch[r] + 1;
+    }
+    return ONELA_OK;
+}
+
 onela_status onela_reset(onela_ctx* ctx, int32_t req) {
     if (!ctx || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;

@@ -61,7 +61,28 @@ struct FullStateParams {
     int32_t epoch[kMaxReqPerLaunch];
 };
 
+// The prefill: one workgroup per (sequence, head) folds a prompt into a state.
+struct PrefillParams {
+    const uint16_t* k;       // bf16 [n_seq][L][H][DK]
+    const uint16_t* v;       // bf16 [n_seq][L][H][DV]
+    const float* alpha;      // [n_seq][L][H]
+    const float* beta;       // [n_seq][L][H]
+    const float* s_init;     // [n_seq][H][DV][DK] float32, or null (zero state)
+    float* s_out;            // [n_seq][H][DV][DK] float32 (the float32 form)
+    uint16_t* planes;        // [max_requests][H][2][DV*DK] bf16 hi/lo in MFMA fragment order (the plane form)
+    int32_t n_seq, H, L;
+    int32_t slot[kMaxReqPerLaunch];  // plane form: request id of sequence i
+};
+
+// S0 as the step kernel's two bf16 planes: hi = rne(x), lo = rne(x - hi).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
 // Returns hipErrorInvalidValue for unsupported (DK, DV).
+hipError_t launch_prefill(int dk, int dv, bool planes, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fullstate_step(int dk, int dv, const FullStateParams& p, hipStream_t s);
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);

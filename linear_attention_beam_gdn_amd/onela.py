@@ -30,7 +30,7 @@ EXPORTED = (
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
     "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
-    "onela_fs_sync", "onela_fs_get_memory",
+    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill",
 )
 
 
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_fs_sync": (i32, [vp]),
         "onela_fs_get_memory": (i32, [vp, vp]),
         "onela_last_error": (ctypes.c_char_p, [vp]),
+        "onela_init_requests_from_prompts": (i32, [vp, i32, p_i32, i32, vp, vp, vp, vp]),
+        "onela_prefill": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -148,6 +150,21 @@ class Onela:
         c = self.cfg
         p = _ptr(S0, "S0", (self._torch.float32,), (c.num_heads, c.d_v, c.d_k))
         self._check(self.lib.onela_init_request(self._ctx, req, p), "onela_init_request")
+
+    def init_requests_from_prompts(self, reqs, k, v, alpha, beta):
+        """S0 of each listed request folded from its prompt on the GPU: k [n][L][H][d_k],
+        v [n][L][H][d_v] (bf16 bits), alpha, beta [n][L][H] float32."""
+        torch = self._torch
+        c = self.cfg
+        n, L = len(reqs), int(k.shape[1])
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        arr = (ctypes.c_int32 * n)(*[int(r) for r in reqs])
+        st = self.lib.onela_init_requests_from_prompts(
+            self._ctx, n, arr, L,
+            _ptr(k, "k", bf, (n, L, c.num_heads, c.d_k)), _ptr(v, "v", bf, (n, L, c.num_heads, c.d_v)),
+            _ptr(alpha, "alpha", (torch.float32,), (n, L, c.num_heads)),
+            _ptr(beta, "beta", (torch.float32,), (n, L, c.num_heads)))
+        self._check(st, "onela_init_requests_from_prompts")
 
     def step(self, reqs, q, k, v, alpha, beta, parent_idx, o, delta_out=None):
         """Advance the given requests one step. q, k, v: bf16 (or int16/uint16 bits)."""
@@ -277,3 +294,31 @@ class FullState:
         b = ctypes.c_uint64()
         self._check(self.lib.onela_fs_get_memory(self._ctx, ctypes.byref(b)), "onela_fs_get_memory")
         return b.value
+
+
+def prefill(k, v, alpha, beta, S_init=None, out=None, stream=None):
+    """Fold prompts into float32 states on the GPU (onela_prefill).
+
+    k: [n][L][H][d_k] and v: [n][L][H][d_v] bf16 (or int16/uint16 bits); alpha,
+    beta: [n][L][H] float32; S_init: optional [n][H][d_v][d_k] float32. Returns
+    `out` (allocated if None), [n][H][d_v][d_k] float32; out may be S_init.
+    """
+    import torch
+
+    lib = load_library()
+    n, L, H, dk = (int(x) for x in k.shape)
+    dv = int(v.shape[3])
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    f32 = (torch.float32,)
+    if out is None:
+        out = torch.empty((n, H, dv, dk), dtype=torch.float32, device=k.device)
+    stream = stream if stream is not None else torch.cuda.current_stream()
+    st = lib.onela_prefill(
+        n, H, dk, dv, L,
+        _ptr(k, "k", bf, (n, L, H, dk)), _ptr(v, "v", bf, (n, L, H, dv)),
+        _ptr(alpha, "alpha", f32, (n, L, H)), _ptr(beta, "beta", f32, (n, L, H)),
+        _ptr(S_init, "S_init", f32, (n, H, dv, dk), optional=True),
+        _ptr(out, "out", f32, (n, H, dv, dk)), ctypes.c_void_p(stream.cuda_stream))
+    if st != ONELA_OK:
+        raise OnelaError(st, "onela_prefill")
+    return out

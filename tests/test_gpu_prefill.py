@@ -1,0 +1,143 @@
+"""The prefill (prompt -> S0) through the C ABI, against the float64 oracle.
+
+The states are compared with max-abs S_TOL = 5e-5: o = S q with a unit q
+moves by at most ||dS||_max * ||q||_1 <= 5e-5 * sqrt(128) < 6e-4, inside the
+decode step's 1e-3 budget; the end-to-end test checks that budget directly.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+S_TOL = 5e-5
+
+if torch.cuda.is_available():
+    import gpu_harness as gh
+    from linear_attention_beam_gdn_amd import Onela, OnelaError, load_library, prefill
+    from oracle import prompt_state
+    from workload import bf16_bits_to_f32, prompt_tokens, shape_of
+    from workload.gen_device import prompt_tokens_device
+
+
+def _host_tokens(shape, n, L):
+    toks = [prompt_tokens(shape, r, L) for r in range(n)]
+    return {key: np.stack([t[key] for t in toks]) for key in ("k", "v", "alpha", "beta")}
+
+
+def _dev(tok):
+    return [gh.to_dev(tok[key]) for key in ("k", "v", "alpha", "beta")]
+
+
+def _oracle(tok, i, heads=None):
+    sl = slice(None) if heads is None else heads
+    return prompt_state(bf16_bits_to_f32(tok["k"][i][:, sl]), bf16_bits_to_f32(tok["v"][i][:, sl]),
+                        tok["alpha"][i][:, sl], tok["beta"][i][:, sl])
+
+
+@pytest.mark.parametrize("d,L,H,n", [(32, 37, 2, 2), (64, 16, 3, 1), (128, 1, 2, 1), (128, 100, 2, 3)])
+def test_prefill_matches_oracle(d, L, H, n):
+    shape = shape_of(0, name=f"prefill_d{d}", H=H, dk=d, dv=d)
+    tok = _host_tokens(shape, n, L)
+    print(f"[prefill] d={d} L={L} H={H} n={n}", flush=True)
+    out = prefill(*_dev(tok)).cpu().numpy()
+    for i in range(n):
+        err = np.abs(out[i] - _oracle(tok, i)).max()
+        assert err <= S_TOL, (i, err)
+
+
+def test_prefill_prompt_config():
+    """The 1024-token prompt of the W = 256, T = 7 workload (all 16 heads)."""
+    shape = shape_of(2)
+    tok = _host_tokens(shape, 1, shape.prompt_len)
+    print(f"[prefill] {shape.name}", flush=True)
+    out = prefill(*_dev(tok)).cpu().numpy()
+    err = np.abs(out[0] - _oracle(tok, 0)).max()
+    print(f"[prefill] {shape.name}: max-abs err {err:.3e}")
+    assert err <= S_TOL
+
+
+def test_prefill_zero_length_and_split_prompts():
+    shape = shape_of(0, name="prefill_split", H=3, dk=64, dv=64)
+    tok = _host_tokens(shape, 2, 45)
+    k, v, a, b = _dev(tok)
+    # no tokens: the initial state (or zero) comes back unchanged
+    init = torch.randn((2, 3, 64, 64), device=gh.dev())
+    empty = lambda x: x[:, :0].contiguous()
+    assert torch.equal(prefill(empty(k), empty(v), empty(a), empty(b), S_init=init), init)
+    assert torch.count_nonzero(prefill(empty(k), empty(v), empty(a), empty(b))) == 0
+    # 45 tokens at once == 29 then 16 (in place), bit for bit
+    whole = prefill(k, v, a, b)
+    part = lambda x, s: x[:, s].contiguous()
+    first = prefill(part(k, slice(0, 29)), part(v, slice(0, 29)), part(a, slice(0, 29)), part(b, slice(0, 29)))
+    second = prefill(part(k, slice(29, 45)), part(v, slice(29, 45)), part(a, slice(29, 45)),
+                     part(b, slice(29, 45)), S_init=first, out=first)
+    assert torch.equal(whole, second)
+
+
+def test_prompt_init_equals_float32_init_and_decodes_within_budget():
+    """S0 folded into the planes on the GPU == onela_init_request of the
+    prefill's float32 state (bit-identical decode), and the decode outputs
+    match the oracle run from the oracle's own S0 within 1e-3."""
+    shape = shape_of(2, name="prompt_e2e", H=4, T=3, prompt_len=300)
+    ep, S0_oracle = gh.episode(shape)
+    tok = _host_tokens(shape, 1, shape.prompt_len)
+    k, v, a, b = _dev(tok)
+    print(f"[prefill] {shape.name}", flush=True)
+    S_gpu = prefill(k, v, a, b)
+    ref = gh.run_episode(shape, ep, S_gpu.cpu().numpy())
+    lay = Onela(2, shape.H, 128, 128, shape.W, shape.T)
+    lay.init_requests_from_prompts([1], k, v, a, b)
+    o = torch.empty((shape.W, shape.H, 128), dtype=torch.float32, device=gh.dev())
+    for t in range(shape.T):
+        par = gh.to_dev(ep["parents"][t].astype(np.int32)) if t else None
+        lay.step([1], *[gh.to_dev(ep[key][t]) for key in ("q", "k", "v", "alpha", "beta")], par, o)
+        assert np.array_equal(o.cpu().numpy(), ref["o"][t])
+    lay.close()
+    ref["layer"].close()
+    for h in range(shape.H):
+        want = gh.oracle_pair(shape, ep, S0_oracle, 0, h)
+        eo, ed = gh.max_err(ref, want, 0, h, shape.W)
+        assert eo <= gh.TOL and ed <= gh.TOL, (h, eo, ed)
+
+
+def test_prefill_bench_size_sampled():
+    """32 prompts of 5120 tokens, 16 heads, d = 128 in one launch (the S0 of
+    the 32-request bench workload); three (request, head) pairs against the
+    oracle on the same seeded tokens."""
+    shape = shape_of(3, s0="prompt", prompt_len=5120)
+    print(f"[prefill] {shape.name} prompt {shape.prompt_len}", flush=True)
+    toks = prompt_tokens_device(shape, gh.dev())
+    out = prefill(toks["k"], toks["v"], toks["alpha"], toks["beta"])
+    torch.cuda.synchronize()
+    for r, h in [(0, 0), (17, 9), (31, 15)]:
+        host = {key: toks[key][r:r + 1, :, h:h + 1].cpu().numpy() for key in toks}
+        host["k"] = host["k"].view(np.uint16)
+        host["v"] = host["v"].view(np.uint16)
+        want = _oracle(host, 0)[0]
+        err = np.abs(out[r, h].cpu().numpy() - want).max()
+        print(f"[prefill] pair ({r}, {h}): max-abs err {err:.3e}", flush=True)
+        assert err <= S_TOL
+
+
+def test_prefill_bad_arguments():
+    shape = shape_of(0, name="prefill_bad", H=2, dk=32, dv=32)
+    tok = _host_tokens(shape, 1, 8)
+    k, v, a, b = _dev(tok)
+    lib = load_library()
+    out = torch.empty((1, 2, 32, 32), device=gh.dev())
+    ptr = lambda t: t.data_ptr()
+    call = lambda n, dk, L, kk=ptr(k), o=ptr(out): lib.onela_prefill(n, 2, dk, dk, L, kk, ptr(v), ptr(a), ptr(b),
+                                                                     None, o, None)
+    assert call(0, 32, 8) == -1                 # no sequences
+    assert call(1, 32, -1) == -1                # negative length
+    assert call(1, 48, 8) == -7                 # no kernel for d = 48
+    assert call(1, 32, 8, kk=ptr(k) + 2) == -1  # misaligned k
+    assert call(1, 32, 8, o=0) == -1            # no output
+    lay = Onela(2, 2, 32, 32, 8, 3)
+    with pytest.raises(OnelaError):
+        lay.init_requests_from_prompts([0, 0], torch.cat([k, k]), torch.cat([v, v]), torch.cat([a, a]),
+                                       torch.cat([b, b]))   # duplicate request id
+    with pytest.raises(OnelaError):
+        lay.init_requests_from_prompts([2], k, v, a, b)     # request id out of range
+    lay.close()

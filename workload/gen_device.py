@@ -50,6 +50,29 @@ def s0_device(shape: Shape, device) -> torch.Tensor:
     return torch.randn((shape.R, shape.H, shape.dv, shape.dk), generator=g, device=device) * shape.s0_sigma
 
 
+def prompt_tokens_device(shape: Shape, device, length: int | None = None, reqs=None) -> dict:
+    """Prompt tokens of the requests, on `device`, for a prompt-derived S0.
+
+    k: int16 bf16 bits [n][L][H][dk] (L2-normalised); v: [n][L][H][dv];
+    alpha, beta: float32 [n][L][H]. Seeded per request, so a request's
+    prompt does not depend on which other requests are drawn.
+    """
+    L = shape.prompt_len if length is None else length
+    reqs = range(shape.R) if reqs is None else reqs
+    ks, vs, als, bes = [], [], [], []
+    for r in reqs:
+        g = _gen(device, shape.cfg, 3000 + r, 3)
+        x = torch.randn((L, shape.H, shape.dk), generator=g, device=device, dtype=torch.float32)
+        x = x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        ks.append(x.to(torch.bfloat16).view(torch.int16))
+        v = torch.randn((L, shape.H, shape.dv), generator=g, device=device, dtype=torch.float32)
+        vs.append(v.to(torch.bfloat16).view(torch.int16))
+        als.append(torch.sigmoid(torch.randn((L, shape.H), generator=g, device=device) * 0.5 + 2.0))
+        bes.append(torch.sigmoid(torch.randn((L, shape.H), generator=g, device=device)))
+    return {"k": torch.stack(ks), "v": torch.stack(vs),
+            "alpha": torch.stack(als).float().contiguous(), "beta": torch.stack(bes).float().contiguous()}
+
+
 def all_parents(shape: Shape) -> np.ndarray:
     """Parents [T][R][W] int32 (row 0 = -1), drawn on the host like `workload.gen`."""
     return np.stack([parents_for(shape, r) for r in range(shape.R)], axis=1)
