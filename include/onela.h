@@ -95,7 +95,29 @@ typedef struct onela_ctx onela_ctx;
  * order (2*max_requests*W int32). On failure *out is NULL. */
 onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out);
 
-/* Synchronise the stream and free everything the context owns. NULL is OK. */
+/* A context for another GDN layer of the same requests that reads the
+ * ancestry index of `index_owner` instead of keeping its own: the beam tree
+ * is one per request, whatever the number of layers (OneLA abstract: a
+ * lightweight ancestry index tracks each beam's records), so one index
+ * update per decode step serves every layer. cfg may differ from the owner's
+ * in num_heads, d_k, d_v; max_requests, beam_width and max_steps must match
+ * (else ONELA_E_INVALID_ARG; an owner cannot itself share another's index).
+ * The owner's onela_step writes the index; a sharing context's step t of a
+ * request reads the rows the owner's step t-1 wrote, so for every request:
+ *   - the sharing context's step t (t >= 2) runs after the owner's step t-1
+ *     and before the owner's step t+1 (else ONELA_E_BAD_STATE, nothing
+ *     enqueued); when they use different streams the caller orders them;
+ *   - after onela_init_request / onela_reset of a request on the owner, every
+ *     sharing context that had stepped it must restart it too before its next
+ *     step there (else ONELA_E_BAD_STATE).
+ * Allocates what onela_create does minus the ancestry index and order.
+ * Destroy sharing contexts before their owner (onela_destroy of an owner that
+ * still has sharers returns ONELA_E_BAD_STATE and frees nothing). */
+onela_status onela_create_sharing_index(const onela_config* cfg, void* hip_stream, onela_ctx* index_owner,
+                                        onela_ctx** out);
+
+/* Synchronise the stream and free everything the context owns. NULL is OK.
+ * An index owner with live sharing contexts: ONELA_E_BAD_STATE. */
 onela_status onela_destroy(onela_ctx* ctx);
 
 /* Load the shared prompt-derived state of request `req` and rewind it to

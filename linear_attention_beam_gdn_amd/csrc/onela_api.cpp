@@ -31,6 +31,11 @@ struct onela_ctx {
     int32_t beams_per_block = 0;     // 0 = automatic
     std::string last_error;
     uint64_t s0_bytes = 0, rec_bytes = 0, idx_bytes = 0;
+    // Layers of one model share one ancestry index: the owner allocates and
+    // writes it, every sharing context only reads it.
+    onela_ctx* index_owner = nullptr;
+    std::vector<onela_ctx*> sharers;
+    std::vector<char> stale;         // the owner restarted the request; this context must too
 };
 
 namespace {
@@ -44,6 +49,16 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_req(const onela_ctx* ctx, int32_t req) {
     return req >= 0 && req < ctx->cfg.max_requests;
+}
+
+// Request `req` starts a new episode on this context (init or reset).
+void restart(onela_ctx* ctx, int32_t req) {
+    ctx->steps[req] = 0;
+    ctx->poisoned[req] = 0;
+    ctx->stale[req] = 0;
+    ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
+    for (onela_ctx* s : ctx->sharers)            // their copies of the episode no longer match the index
+        if (s->steps[req] > 0) s->stale[req] = 1;
 }
 
 // Copy the device error words to the host and poison every flagged request.
@@ -89,7 +104,7 @@ const char* onela_status_string(onela_status s) {
 
 const char* onela_last_error(const onela_ctx* ctx) { return ctx ? ctx->last_error.c_str() : ""; }
 
-onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out) {
+static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_ctx* owner, onela_ctx** out) {
     if (!out) return ONELA_E_INVALID_ARG;
     *out = nullptr;
     if (!cfg || cfg->max_requests < 1 || cfg->num_heads < 1 || cfg->beam_width < 1 || cfg->max_steps < 1 ||
@@ -113,25 +128,32 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
     const uint64_t nrec = R * H * T * W;
     ctx->s0_bytes = R * H * 2 * dv * dk * 2;
     ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
-    ctx->idx_bytes = 2 * R * W * T * 4 + 2 * R * W * 4 + R * 4;
+    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + R * 4;
 
     bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
               hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
               hipMalloc(&ctx->rec_delta, nrec * 4 * dv) == hipSuccess &&
               hipMalloc(&ctx->rec_k, nrec * 2 * dk) == hipSuccess &&
-              hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess &&
-              hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess &&
               hipMalloc(&ctx->err, R * 4) == hipSuccess;
+    if (ok && !owner)
+        ok = hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess && hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess;
     if (!ok) {
         (void)hipGetLastError();
         onela_destroy(ctx);
         return ONELA_E_OOM;
     }
     if (hipMemsetAsync(ctx->err, 0, R * 4, ctx->stream) != hipSuccess ||
-        hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess) {
+        (!owner && hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess)) {
         onela_destroy(ctx);
         return ONELA_E_HIP;
     }
+    if (owner) {
+        ctx->anc = owner->anc;
+        ctx->order = owner->order;
+        ctx->index_owner = owner;
+        owner->sharers.push_back(ctx);
+    }
+    ctx->stale.assign(R, 0);
     ctx->steps.assign(R, -1);
     ctx->poisoned.assign(R, 0);
     ctx->err_host.assign(R, 0);
@@ -140,15 +162,36 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
     return ONELA_OK;
 }
 
+onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out) {
+    return create_ctx(cfg, hip_stream, nullptr, out);
+}
+
+onela_status onela_create_sharing_index(const onela_config* cfg, void* hip_stream, onela_ctx* index_owner,
+                                        onela_ctx** out) {
+    if (!out) return ONELA_E_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg || !index_owner || index_owner->index_owner) return ONELA_E_INVALID_ARG;
+    const auto& oc = index_owner->cfg;
+    if (cfg->max_requests != oc.max_requests || cfg->beam_width != oc.beam_width || cfg->max_steps != oc.max_steps)
+        return ONELA_E_INVALID_ARG;
+    return create_ctx(cfg, hip_stream, index_owner, out);
+}
+
 onela_status onela_destroy(onela_ctx* ctx) {
     if (!ctx) return ONELA_OK;
+    if (!ctx->sharers.empty()) return ONELA_E_BAD_STATE;     // sharing contexts go first
     (void)hipStreamSynchronize(ctx->stream);
     (void)hipFree(ctx->s0_planes);
     (void)hipFree(ctx->rec_alpha);
     (void)hipFree(ctx->rec_delta);
     (void)hipFree(ctx->rec_k);
-    (void)hipFree(ctx->anc);
-    (void)hipFree(ctx->order);
+    if (ctx->index_owner) {
+        auto& v = ctx->index_owner->sharers;
+        v.erase(std::remove(v.begin(), v.end(), ctx), v.end());
+    } else {
+        (void)hipFree(ctx->anc);
+        (void)hipFree(ctx->order);
+    }
     (void)hipFree(ctx->err);
     delete ctx;
     return ONELA_OK;
@@ -160,9 +203,7 @@ onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0) {
     uint16_t* planes = ctx->s0_planes + (size_t)req * c.num_heads * 2 * c.d_v * c.d_k;
     hipError_t e = onela::launch_init_s0(c.d_k, c.d_v, S0, planes, c.num_heads, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "init_s0 launch");
-    ctx->steps[req] = 0;
-    ctx->poisoned[req] = 0;
-    ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
+    restart(ctx, req);
     return ONELA_OK;
 }
 
@@ -196,21 +237,14 @@ onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, con
         hipError_t e = onela::launch_prefill(c.d_k, c.d_v, true, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
     }
-    for (int i = 0; i < n_req; ++i) {
-        const int r = reqs[i];
-        ctx->steps[r] = 0;
-        ctx->poisoned[r] = 0;
-        ctx->epoch[r] = ctx->epoch[r] == INT32_MAX ? 1 : ctx->epoch[r] + 1;
-    }
+    for (int i = 0; i < n_req; ++i) restart(ctx, reqs[i]);
     return ONELA_OK;
 }
 
 onela_status onela_reset(onela_ctx* ctx, int32_t req) {
     if (!ctx || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
-    ctx->steps[req] = 0;
-    ctx->poisoned[req] = 0;
-    ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
+    restart(ctx, req);
     return ONELA_OK;
 }
 
@@ -236,9 +270,16 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         const int r = reqs[i];
         if (!valid_req(ctx, r) || seen[r]) return ONELA_E_INVALID_ARG;
         seen[r] = 1;
-        if (ctx->steps[r] < 0 || ctx->poisoned[r]) return ONELA_E_BAD_STATE;
+        if (ctx->steps[r] < 0 || ctx->poisoned[r] || ctx->stale[r]) return ONELA_E_BAD_STATE;
         if (ctx->steps[r] >= c.max_steps) return ONELA_E_CAPACITY;
         if (ctx->steps[r] >= 1) need_parents = true;
+        const int t = ctx->steps[r] + 1;
+        // shared index: step t reads the rows the owner's step t-1 wrote, which
+        // the owner's step t+1 overwrites
+        if (ctx->index_owner && t >= 2 && ctx->index_owner->steps[r] != t - 1 && ctx->index_owner->steps[r] != t)
+            return ONELA_E_BAD_STATE;
+        for (const onela_ctx* sh : ctx->sharers)
+            if (t >= 2 && sh->steps[r] >= 1 && !sh->stale[r] && sh->steps[r] < t - 1) return ONELA_E_BAD_STATE;
     }
     if (need_parents && !parent_idx) return ONELA_E_INVALID_ARG;
 
@@ -250,6 +291,7 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
     p.anc = ctx->anc;
     p.order = ctx->order;
     p.err = ctx->err;
+    p.write_index = ctx->index_owner ? 0 : 1;
     p.H = c.num_heads;
     p.W = c.beam_width;
     p.T_max = c.max_steps;

@@ -33,6 +33,7 @@ struct StepParams {
     int32_t* order;             // [2][max_requests][W] beam processing order (ping-pong by step parity)
     int32_t* err;               // [max_requests]: epoch of the last step that saw a bad parent
     int32_t H, W, T_max, max_requests;
+    int32_t write_index;        // 1: this launch writes the next step's ancestry rows and order
     int32_t beams_per_block;    // multiple of kChunk, or >= W
     int32_t n_splits;           // ceil(W / beams_per_block)
     int32_t n_req;

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             }
         }
         lds_barrier();
-        if (h == 0 && split == 0)
+        if (p.write_index && h == 0 && split == 0)
             for (int i = tid; i < W; i += NT) ord_next[i] = ord_s[i];
     }
     auto beam_at = [&](int i) __attribute__((always_inline)) { return ordered ? ord_s[i] : i; };
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // head) cover [0, W) between them), so the small writes coalesce.
     for (int b = b_begin + tid; b < b_end; b += NT) {
         ralpha[depth * W + b] = ain[b * H];
-        if (h == 0 && depth > 0) {                     // one head writes the index
+        if (p.write_index && h == 0 && depth > 0) {   // one head of the index owner writes it
             int pb = parin[b];
             pb = (pb < 0 || pb >= W) ? 0 : pb;         // (reported in phase A)
             for (int j = 0; j + 1 < depth; ++j) anc_next[b * p.T_max + j] = anc_prev[pb * p.T_max + j];

@@ -30,7 +30,7 @@ EXPORTED = (
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
     "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
-    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill",
+    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index",
 )
 
 
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_last_error": (ctypes.c_char_p, [vp]),
         "onela_init_requests_from_prompts": (i32, [vp, i32, p_i32, i32, vp, vp, vp, vp]),
         "onela_prefill": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "onela_create_sharing_index": (i32, [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -109,7 +110,9 @@ def _ptr(t, name, dtype=None, shape=None, optional=False):
 class Onela:
     """One GDN layer's OneLA decode state on the current HIP device."""
 
-    def __init__(self, max_requests, num_heads, d_k, d_v, beam_width, max_steps, stream=None):
+    def __init__(self, max_requests, num_heads, d_k, d_v, beam_width, max_steps, stream=None, share_index_of=None):
+        """share_index_of: another Onela (a layer of the same requests) whose
+        ancestry index this layer reads instead of keeping its own."""
         import torch
 
         self._torch = torch
@@ -117,8 +120,14 @@ class Onela:
         self.cfg = _Config(max_requests, num_heads, d_k, d_v, beam_width, max_steps)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._ctx = ctypes.c_void_p()
-        self._check(self.lib.onela_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.stream.cuda_stream),
-                                          ctypes.byref(self._ctx)), "onela_create")
+        self.index_owner = share_index_of
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        if share_index_of is None:
+            st = self.lib.onela_create(ctypes.byref(self.cfg), s, ctypes.byref(self._ctx))
+        else:
+            st = self.lib.onela_create_sharing_index(ctypes.byref(self.cfg), s, share_index_of._ctx,
+                                                     ctypes.byref(self._ctx))
+        self._check(st, "onela_create")
 
     # -- helpers --------------------------------------------------------------
     def _check(self, status, where):
@@ -130,7 +139,7 @@ class Onela:
 
     def close(self):
         if self._ctx:
-            self.lib.onela_destroy(self._ctx)
+            self._check(self.lib.onela_destroy(self._ctx), "onela_destroy")
             self._ctx = ctypes.c_void_p()
 
     def __enter__(self):
