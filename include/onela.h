@@ -188,6 +188,27 @@ onela_status onela_reset(onela_ctx* ctx, int32_t req);
  * poisoned by a bad parent index, ONELA_E_HIP on a HIP failure. */
 onela_status onela_sync(onela_ctx* ctx);
 
+/* Graph mode on (1) or off (0). In graph mode each request's step index and
+ * episode number live in device memory and every onela_step enqueues the
+ * step launch plus a one-workgroup launch that advances the step counters,
+ * so the launches of a decode step (of every layer) can be captured once in
+ * a HIP graph and replayed for the following decode steps, the caller
+ * refilling the same input buffers before each replay (the pages' serving
+ * loop is decode-forward, OneLA review, evolve.pub, "Summary"). In this mode:
+ *   - onela_step requires parent_idx (ignored for requests at t = 1) and
+ *     does no step-count checks on the host; a step past max_steps is found
+ *     on the device, writes nothing, and makes the next onela_sync return
+ *     ONELA_E_CAPACITY (cleared by onela_reset / onela_init_request);
+ *   - the host ordering checks of a shared index are off: step every layer
+ *     of a decode step, owner first, as the eager calls would;
+ *   - onela_reset and onela_init_request enqueue a small counter write, so
+ *     they belong outside captured graphs;
+ *   - getters and onela_sync refresh the host's step counters from the
+ *     device.
+ * Switching synchronises the stream. Default: off (step counters on the
+ * host, onela_reset enqueues nothing). */
+onela_status onela_set_graph_mode(onela_ctx* ctx, int32_t on);
+
 /* Beams handled by one workgroup (0 = automatic). Must be 0 or a multiple of
  * 64. Results do not depend on it; only the launch shape does. */
 onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
@@ -207,7 +228,10 @@ onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out);
 onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_t n_rec,
                                float* alpha, float* delta, uint16_t* key);
 
-/* Device bytes the context owns: S0 planes, record store, ancestry index. */
+/* Device bytes the context owns: S0 planes, record store, and in index_bytes
+ * the ancestry index and beam order (none on a context sharing another's
+ * index) plus four int32 words per request (error words, graph-mode
+ * counters). */
 onela_status onela_get_memory(const onela_ctx* ctx, uint64_t* s0_bytes,
                               uint64_t* record_bytes, uint64_t* index_bytes);
 

@@ -36,6 +36,13 @@ struct onela_ctx {
     onela_ctx* index_owner = nullptr;
     std::vector<onela_ctx*> sharers;
     std::vector<char> stale;         // the owner restarted the request; this context must too
+    // Graph mode: the device holds each request's step and episode number, so
+    // captured onela_step launches advance correctly on every replay.
+    bool graph_mode = false;
+    int32_t* dev_steps = nullptr;    // [R]
+    int32_t* dev_epoch = nullptr;    // [R]
+    int32_t* err_cap = nullptr;      // [R]
+    std::vector<char> capacity_hit;  // a graph-mode step ran past max_steps
 };
 
 namespace {
@@ -51,25 +58,41 @@ bool valid_req(const onela_ctx* ctx, int32_t req) {
     return req >= 0 && req < ctx->cfg.max_requests;
 }
 
-// Request `req` starts a new episode on this context (init or reset).
-void restart(onela_ctx* ctx, int32_t req) {
+// Request `req` starts a new episode on this context (init or reset); the
+// device copies of its counters follow on the stream.
+hipError_t restart(onela_ctx* ctx, int32_t req) {
     ctx->steps[req] = 0;
     ctx->poisoned[req] = 0;
     ctx->stale[req] = 0;
+    ctx->capacity_hit[req] = 0;
     ctx->epoch[req] = ctx->epoch[req] == INT32_MAX ? 1 : ctx->epoch[req] + 1;
     for (onela_ctx* s : ctx->sharers)            // their copies of the episode no longer match the index
         if (s->steps[req] > 0) s->stale[req] = 1;
+    if (!ctx->graph_mode) return hipSuccess;     // host-only outside graph mode
+    return onela::launch_set_counters(ctx->dev_steps, ctx->dev_epoch, req, 0, ctx->epoch[req], ctx->stream);
 }
 
-// Copy the device error words to the host and poison every flagged request.
+// Copy the device error words to the host and poison every flagged request;
+// in graph mode also take the device's step counters as the host's.
 onela_status drain(onela_ctx* ctx) {
+    const size_t bytes = sizeof(int32_t) * ctx->cfg.max_requests;
     hipError_t e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
-    e = hipMemcpy(ctx->err_host.data(), ctx->err, sizeof(int32_t) * ctx->cfg.max_requests,
-                  hipMemcpyDeviceToHost);
+    e = hipMemcpy(ctx->err_host.data(), ctx->err, bytes, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(err)");
     for (int r = 0; r < ctx->cfg.max_requests; ++r)
         if (ctx->err_host[r] != 0 && ctx->err_host[r] == ctx->epoch[r]) ctx->poisoned[r] = 1;
+    if (ctx->graph_mode) {
+        e = hipMemcpy(ctx->err_host.data(), ctx->err_cap, bytes, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(err_cap)");
+        for (int r = 0; r < ctx->cfg.max_requests; ++r)
+            if (ctx->err_host[r] != 0 && ctx->err_host[r] == ctx->epoch[r]) ctx->capacity_hit[r] = 1;
+        std::vector<int32_t> dsteps(ctx->cfg.max_requests);
+        e = hipMemcpy(dsteps.data(), ctx->dev_steps, bytes, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(steps)");
+        for (int r = 0; r < ctx->cfg.max_requests; ++r)
+            if (ctx->steps[r] >= 0) ctx->steps[r] = dsteps[r];
+    }
     return ONELA_OK;
 }
 
@@ -128,13 +151,14 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
     const uint64_t nrec = R * H * T * W;
     ctx->s0_bytes = R * H * 2 * dv * dk * 2;
     ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
-    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + R * 4;
+    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + 4 * R * 4;   // + error words, counters
 
     bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
               hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
               hipMalloc(&ctx->rec_delta, nrec * 4 * dv) == hipSuccess &&
               hipMalloc(&ctx->rec_k, nrec * 2 * dk) == hipSuccess &&
-              hipMalloc(&ctx->err, R * 4) == hipSuccess;
+              hipMalloc(&ctx->err, R * 4) == hipSuccess && hipMalloc(&ctx->dev_steps, R * 4) == hipSuccess &&
+              hipMalloc(&ctx->dev_epoch, R * 4) == hipSuccess && hipMalloc(&ctx->err_cap, R * 4) == hipSuccess;
     if (ok && !owner)
         ok = hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess && hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess;
     if (!ok) {
@@ -143,7 +167,11 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
         return ONELA_E_OOM;
     }
     if (hipMemsetAsync(ctx->err, 0, R * 4, ctx->stream) != hipSuccess ||
-        (!owner && hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess)) {
+        hipMemsetAsync(ctx->err_cap, 0, R * 4, ctx->stream) != hipSuccess ||
+        hipMemsetAsync(ctx->dev_steps, 0, R * 4, ctx->stream) != hipSuccess ||
+        hipMemsetAsync(ctx->dev_epoch, 0, R * 4, ctx->stream) != hipSuccess ||
+        (!owner && hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess) ||
+        onela::prepare_step(cfg->d_k, cfg->d_v, cfg->max_steps, cfg->beam_width) != hipSuccess) {
         onela_destroy(ctx);
         return ONELA_E_HIP;
     }
@@ -154,6 +182,7 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
         owner->sharers.push_back(ctx);
     }
     ctx->stale.assign(R, 0);
+    ctx->capacity_hit.assign(R, 0);
     ctx->steps.assign(R, -1);
     ctx->poisoned.assign(R, 0);
     ctx->err_host.assign(R, 0);
@@ -193,6 +222,9 @@ onela_status onela_destroy(onela_ctx* ctx) {
         (void)hipFree(ctx->order);
     }
     (void)hipFree(ctx->err);
+    (void)hipFree(ctx->dev_steps);
+    (void)hipFree(ctx->dev_epoch);
+    (void)hipFree(ctx->err_cap);
     delete ctx;
     return ONELA_OK;
 }
@@ -203,8 +235,8 @@ onela_status onela_init_request(onela_ctx* ctx, int32_t req, const float* S0) {
     uint16_t* planes = ctx->s0_planes + (size_t)req * c.num_heads * 2 * c.d_v * c.d_k;
     hipError_t e = onela::launch_init_s0(c.d_k, c.d_v, S0, planes, c.num_heads, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "init_s0 launch");
-    restart(ctx, req);
-    return ONELA_OK;
+    e = restart(ctx, req);
+    return e == hipSuccess ? ONELA_OK : hip_fail(ctx, e, "counter launch");
 }
 
 onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, int32_t seq_len,
@@ -237,14 +269,35 @@ onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, con
         hipError_t e = onela::launch_prefill(c.d_k, c.d_v, true, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "prefill launch");
     }
-    for (int i = 0; i < n_req; ++i) restart(ctx, reqs[i]);
+    for (int i = 0; i < n_req; ++i) {
+        hipError_t e = restart(ctx, reqs[i]);
+        if (e != hipSuccess) return hip_fail(ctx, e, "counter launch");
+    }
     return ONELA_OK;
 }
 
 onela_status onela_reset(onela_ctx* ctx, int32_t req) {
     if (!ctx || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
-    restart(ctx, req);
+    hipError_t e = restart(ctx, req);
+    return e == hipSuccess ? ONELA_OK : hip_fail(ctx, e, "counter launch");
+}
+
+onela_status onela_set_graph_mode(onela_ctx* ctx, int32_t on) {
+    if (!ctx || (on != 0 && on != 1)) return ONELA_E_INVALID_ARG;
+    if ((bool)on == ctx->graph_mode) return ONELA_OK;
+    onela_status st = drain(ctx);                 // (leaving graph mode: takes the device's step counters)
+    if (st != ONELA_OK) return st;
+    if (on) {
+        const size_t bytes = sizeof(int32_t) * ctx->cfg.max_requests;
+        std::vector<int32_t> zero(ctx->cfg.max_requests, 0), steps(ctx->steps);
+        for (auto& x : steps) x = std::max(x, 0);
+        hipError_t e = hipMemcpy(ctx->dev_steps, steps.data(), bytes, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(ctx->dev_epoch, ctx->epoch.data(), bytes, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(ctx->err_cap, zero.data(), bytes, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(counters)");
+    }
+    ctx->graph_mode = on;
     return ONELA_OK;
 }
 
@@ -271,6 +324,11 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         if (!valid_req(ctx, r) || seen[r]) return ONELA_E_INVALID_ARG;
         seen[r] = 1;
         if (ctx->steps[r] < 0 || ctx->poisoned[r] || ctx->stale[r]) return ONELA_E_BAD_STATE;
+        if (ctx->graph_mode) {                    // the step index is known on the device only
+            if (ctx->capacity_hit[r]) return ONELA_E_CAPACITY;
+            need_parents = true;
+            continue;
+        }
         if (ctx->steps[r] >= c.max_steps) return ONELA_E_CAPACITY;
         if (ctx->steps[r] >= 1) need_parents = true;
         const int t = ctx->steps[r] + 1;
@@ -292,6 +350,9 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
     p.order = ctx->order;
     p.err = ctx->err;
     p.write_index = ctx->index_owner ? 0 : 1;
+    p.dev_steps = ctx->graph_mode ? ctx->dev_steps : nullptr;
+    p.dev_epoch = ctx->dev_epoch;
+    p.err_cap = ctx->err_cap;
     p.H = c.num_heads;
     p.W = c.beam_width;
     p.T_max = c.max_steps;
@@ -318,7 +379,17 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         }
         hipError_t e = onela::launch_step(c.d_k, c.d_v, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
-        for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;
+        if (ctx->graph_mode) {
+            onela::AdvanceParams a{};
+            a.dev_steps = ctx->dev_steps;
+            a.T_max = c.max_steps;
+            a.n = n;
+            for (int i = 0; i < n; ++i) a.slot[i] = p.slot[i];
+            e = onela::launch_advance(a, ctx->stream);
+            if (e != hipSuccess) return hip_fail(ctx, e, "advance launch");
+        } else {
+            for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;
+        }
     }
     return ONELA_OK;
 }
@@ -329,6 +400,8 @@ onela_status onela_sync(onela_ctx* ctx) {
     if (s != ONELA_OK) return s;
     for (int r = 0; r < ctx->cfg.max_requests; ++r)
         if (ctx->poisoned[r]) return ONELA_E_PARENT_RANGE;
+    for (int r = 0; r < ctx->cfg.max_requests; ++r)
+        if (ctx->capacity_hit[r]) return ONELA_E_CAPACITY;
     return ONELA_OK;
 }
 
@@ -368,9 +441,9 @@ onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_
         return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
     const auto& c = ctx->cfg;
-    if ((int64_t)n_rec > (int64_t)ctx->steps[req] * c.beam_width) return ONELA_E_INVALID_ARG;
-    onela_status s = drain(ctx);
+    onela_status s = drain(ctx);                  // (graph mode: refreshes the step counters)
     if (s != ONELA_OK) return s;
+    if ((int64_t)n_rec > (int64_t)ctx->steps[req] * c.beam_width) return ONELA_E_INVALID_ARG;
     if (ctx->poisoned[req]) return ONELA_E_PARENT_RANGE;
     const size_t rec0 = ((size_t)req * c.num_heads + head) * (size_t)c.max_steps * c.beam_width;
     hipError_t e = hipSuccess;

@@ -144,7 +144,15 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     const int ri = pair / p.H;
     const int h = pair % p.H;
     const int slot = p.slot[ri];
-    const int t = p.t[ri];
+    int t = p.t[ri], epoch = p.epoch[ri];
+    if (p.dev_steps) {                            // graph mode: the counters live on the device
+        t = p.dev_steps[slot] + 1;
+        epoch = p.dev_epoch[slot];
+        if (t > p.T_max) {                        // no record slot left: report, write nothing
+            if (threadIdx.x == 0) p.err_cap[slot] = epoch;
+            return;
+        }
+    }
     const int H = p.H, W = p.W;
     const int depth = t - 1;                      // ancestral records per beam
     const int b_begin = split * p.beams_per_block;
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         const bool beam_thread = tid_l < nb;                   // one thread per beam of the chunk
         if (beam_thread && depth > 0) {
             if (par < 0 || par >= W) {                       // reported through the error word
-                p.err[slot] = p.epoch[ri];
+                p.err[slot] = epoch;
                 par = 0;
             }
             const int* src = anc_prev + par * p.T_max;
@@ -539,16 +547,34 @@ hipError_t launch_init_t(const float* S0, uint16_t* planes, int H, hipStream_t s
 }
 
 template <int DK, int DV>
+hipError_t prepare_step_t(int T_max, int W) {
+    const size_t lds = step_lds_bytes(DK, DV, T_max, W);
+    if (lds <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int DK, int DV>
 hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
     const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     const int nblk = p.n_req * p.H * p.n_splits;
     hipLaunchKernelGGL((step_kernel<DK, DV>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
     return hipGetLastError();
+}
+
+__global__ __launch_bounds__(64) void advance_kernel(const AdvanceParams a) {
+    const int i = threadIdx.x;
+    if (i < a.n) {
+        const int c = a.dev_steps[a.slot[i]];
+        a.dev_steps[a.slot[i]] = c < a.T_max ? c + 1 : c;
+    }
+}
+
+__global__ __launch_bounds__(64) void set_counters_kernel(int32_t* steps, int32_t* epoch, int req, int sv, int ev) {
+    if (threadIdx.x == 0) {
+        steps[req] = sv;
+        epoch[req] = ev;
+    }
 }
 
 }  // namespace
@@ -572,6 +598,25 @@ hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int
     if (dk == 64 && dv == 64) return launch_init_t<64, 64>(S0, planes, H, s);
     if (dk == 128 && dv == 128) return launch_init_t<128, 128>(S0, planes, H, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t prepare_step(int dk, int dv, int T_max, int W) {
+    if (dk == 32 && dv == 32) return prepare_step_t<32, 32>(T_max, W);
+    if (dk == 64 && dv == 64) return prepare_step_t<64, 64>(T_max, W);
+    if (dk == 128 && dv == 128) return prepare_step_t<128, 128>(T_max, W);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_advance(const AdvanceParams& a, hipStream_t s) {
+    hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, int steps_value, int epoch_value,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(set_counters_kernel, dim3(1), dim3(64), 0, s, dev_steps, dev_epoch, req, steps_value,
+                       epoch_value);
+    return hipGetLastError();
 }
 
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s) {

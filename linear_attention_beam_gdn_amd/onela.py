@@ -30,7 +30,7 @@ EXPORTED = (
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
     "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
-    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index",
+    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode",
 )
 
 
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_init_requests_from_prompts": (i32, [vp, i32, p_i32, i32, vp, vp, vp, vp]),
         "onela_prefill": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "onela_create_sharing_index": (i32, [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp)]),
+        "onela_set_graph_mode": (i32, [vp, i32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -202,6 +203,10 @@ class Onela:
 
     def sync(self):
         self._check(self.lib.onela_sync(self._ctx), "onela_sync")
+
+    def set_graph_mode(self, on: bool):
+        """Step counters on the device, so captured onela_step launches replay correctly."""
+        self._check(self.lib.onela_set_graph_mode(self._ctx, int(bool(on))), "onela_set_graph_mode")
 
     def set_beams_per_block(self, beams: int):
         self._check(self.lib.onela_set_beams_per_block(self._ctx, beams), "onela_set_beams_per_block")
