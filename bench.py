@@ -190,6 +190,75 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     }
 
 
+def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
+    """A decode step of n_layers GDN layers sharing one ancestry index, eager vs
+    one HIP graph per decode step (graph mode: step counters on the device).
+
+    Every layer gets the same inputs (the cost does not depend on their
+    values). Returns microseconds per decode step (all layers), medians over
+    the episodes, per depth and on average.
+    """
+    import torch
+
+    from linear_attention_beam_gdn_amd import Onela
+
+    R, H, W, T = shape.R, shape.H, shape.W, shape.T
+    s = torch.cuda.Stream()
+    layers = [Onela(R, H, shape.dk, shape.dv, W, T, stream=s)]
+    layers += [Onela(R, H, shape.dk, shape.dv, W, T, stream=s, share_index_of=layers[0]) for _ in range(n_layers - 1)]
+    reqs = list(range(R))
+    outs = [torch.empty((R * W, H, shape.dv), dtype=torch.float32, device=q[0].device) for _ in layers]
+    for lay in layers:
+        for r in reqs:
+            lay.init_request(r, S0[r].contiguous())
+
+    def decode_step(t):
+        for lay, o in zip(layers, outs):
+            lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t] if t else par[1], o)
+
+    def run(replay):
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+        per = []
+        for it in range(episodes + 2):
+            for lay in layers:
+                for r in reqs:
+                    lay.reset(r)
+            for t in range(T):
+                ev[t][0].record(s)
+                replay(t)
+                ev[t][1].record(s)
+            s.synchronize()
+            if it >= 2:
+                per.append([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(T)])
+        for lay in layers:
+            lay.sync()
+        return np.median(np.array(per), axis=0)
+
+    with torch.cuda.stream(s):
+        eager = run(decode_step)
+        for lay in layers:
+            lay.set_graph_mode(True)
+        graphs = []
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                decode_step(t)
+            graphs.append(g)
+        graph = run(lambda t: graphs[t].replay())
+    del graphs
+    for lay in reversed(layers):
+        lay.close()
+    return {
+        "what": f"one decode step of {n_layers} GDN layers sharing one ancestry index (all {R} requests), "
+                "eager onela_step calls vs one captured HIP graph per decode step",
+        "layers": n_layers,
+        "eager_us_per_decode_step": float(eager.mean()),
+        "graph_us_per_decode_step": float(graph.mean()),
+        "eager_us_by_depth": [round(float(x), 1) for x in eager],
+        "graph_us_by_depth": [round(float(x), 1) for x in graph],
+    }
+
+
 def fullstate_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela_ms_per_step, onela_mem):
     """Same workload through the full-state comparator (a full state per beam)."""
     import torch
@@ -303,6 +372,8 @@ def main():
     ap.add_argument("--s0", choices=("prompt", "normal"), default="prompt",
                     help="S0 folded on the GPU from a synthetic prompt (default) or drawn N(0, 0.05^2)")
     ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layers of the multi-layer decode-step leg (eager vs HIP graph); 0 skips it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB first (reference for hardware traffic counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -356,7 +427,7 @@ def main():
     prefill_out = None
     if args.s0 == "prompt":
         S0_dev, prefill_out = prompt_s0(lay, shape, args.prompt_len, reqs, dev, stream,
-                                        need_f32=not args.no_fullstate)
+                                        need_f32=not args.no_fullstate or args.layers > 0)
         s0_label = (f"prompt-derived: the GDN recurrence over {args.prompt_len} synthetic tokens per request "
                     "and head, folded on the GPU (prefill_kernel)")
     else:
@@ -449,6 +520,9 @@ def main():
         out["prefill"] = prefill_out
     mem = lay.memory()
     lay.close()
+    if args.layers > 0:
+        S0_ml = S0_dev if S0_dev is not None else up(ep["S0"])
+        out["multi_layer"] = multi_layer_leg(shape, args.layers, q, k, v, al, be, par, S0_ml)
     if not args.no_fullstate:
         out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o,
                                                     up(ep["S0"]) if S0_dev is None else S0_dev, stream,

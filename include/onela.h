@@ -189,9 +189,9 @@ onela_status onela_reset(onela_ctx* ctx, int32_t req);
 onela_status onela_sync(onela_ctx* ctx);
 
 /* Graph mode on (1) or off (0). In graph mode each request's step index and
- * episode number live in device memory and every onela_step enqueues the
- * step launch plus a one-workgroup launch that advances the step counters,
- * so the launches of a decode step (of every layer) can be captured once in
+ * episode number live in device memory and each step launch advances them
+ * itself (the last workgroup of a request to finish), so the launches of a
+ * decode step (of every layer) can be captured once in
  * a HIP graph and replayed for the following decode steps, the caller
  * refilling the same input buffers before each replay (the pages' serving
  * loop is decode-forward, OneLA review, evolve.pub, "Summary"). In this mode:
@@ -230,7 +230,7 @@ onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_
 
 /* Device bytes the context owns: S0 planes, record store, and in index_bytes
  * the ancestry index and beam order (none on a context sharing another's
- * index) plus four int32 words per request (error words, graph-mode
+ * index) plus five int32 words per request (error words, graph-mode
  * counters). */
 onela_status onela_get_memory(const onela_ctx* ctx, uint64_t* s0_bytes,
                               uint64_t* record_bytes, uint64_t* index_bytes);

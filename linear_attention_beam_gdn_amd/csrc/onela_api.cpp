@@ -42,6 +42,7 @@ struct onela_ctx {
     int32_t* dev_steps = nullptr;    // [R]
     int32_t* dev_epoch = nullptr;    // [R]
     int32_t* err_cap = nullptr;      // [R]
+    int32_t* done = nullptr;         // [R] finished workgroups of the running launch (0 between launches)
     std::vector<char> capacity_hit;  // a graph-mode step ran past max_steps
 };
 
@@ -151,14 +152,15 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
     const uint64_t nrec = R * H * T * W;
     ctx->s0_bytes = R * H * 2 * dv * dk * 2;
     ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
-    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + 4 * R * 4;   // + error words, counters
+    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + 5 * R * 4;   // + error words, counters
 
     bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
               hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
               hipMalloc(&ctx->rec_delta, nrec * 4 * dv) == hipSuccess &&
               hipMalloc(&ctx->rec_k, nrec * 2 * dk) == hipSuccess &&
               hipMalloc(&ctx->err, R * 4) == hipSuccess && hipMalloc(&ctx->dev_steps, R * 4) == hipSuccess &&
-              hipMalloc(&ctx->dev_epoch, R * 4) == hipSuccess && hipMalloc(&ctx->err_cap, R * 4) == hipSuccess;
+              hipMalloc(&ctx->dev_epoch, R * 4) == hipSuccess && hipMalloc(&ctx->err_cap, R * 4) == hipSuccess &&
+              hipMalloc(&ctx->done, R * 4) == hipSuccess;
     if (ok && !owner)
         ok = hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess && hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess;
     if (!ok) {
@@ -168,6 +170,7 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
     }
     if (hipMemsetAsync(ctx->err, 0, R * 4, ctx->stream) != hipSuccess ||
         hipMemsetAsync(ctx->err_cap, 0, R * 4, ctx->stream) != hipSuccess ||
+        hipMemsetAsync(ctx->done, 0, R * 4, ctx->stream) != hipSuccess ||
         hipMemsetAsync(ctx->dev_steps, 0, R * 4, ctx->stream) != hipSuccess ||
         hipMemsetAsync(ctx->dev_epoch, 0, R * 4, ctx->stream) != hipSuccess ||
         (!owner && hipMemsetAsync(ctx->anc, 0xff, 2 * R * W * T * 4, ctx->stream) != hipSuccess) ||
@@ -225,6 +228,7 @@ onela_status onela_destroy(onela_ctx* ctx) {
     (void)hipFree(ctx->dev_steps);
     (void)hipFree(ctx->dev_epoch);
     (void)hipFree(ctx->err_cap);
+    (void)hipFree(ctx->done);
     delete ctx;
     return ONELA_OK;
 }
@@ -353,6 +357,7 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
     p.dev_steps = ctx->graph_mode ? ctx->dev_steps : nullptr;
     p.dev_epoch = ctx->dev_epoch;
     p.err_cap = ctx->err_cap;
+    p.done = ctx->done;
     p.H = c.num_heads;
     p.W = c.beam_width;
     p.T_max = c.max_steps;
@@ -379,17 +384,8 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         }
         hipError_t e = onela::launch_step(c.d_k, c.d_v, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
-        if (ctx->graph_mode) {
-            onela::AdvanceParams a{};
-            a.dev_steps = ctx->dev_steps;
-            a.T_max = c.max_steps;
-            a.n = n;
-            for (int i = 0; i < n; ++i) a.slot[i] = p.slot[i];
-            e = onela::launch_advance(a, ctx->stream);
-            if (e != hipSuccess) return hip_fail(ctx, e, "advance launch");
-        } else {
+        if (!ctx->graph_mode)                     // (graph mode: the launch advances the device counters)
             for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;
-        }
     }
     return ONELA_OK;
 }

@@ -34,9 +34,10 @@ struct StepParams {
     int32_t* err;               // [max_requests]: epoch of the last step that saw a bad parent
     // Graph mode (non-null dev_steps): each request's step and episode number
     // come from device memory, so a captured launch stays valid on replay.
-    const int32_t* dev_steps;   // [max_requests] steps done
+    int32_t* dev_steps;         // [max_requests] steps done; the launch's last workgroup of a request advances it
     const int32_t* dev_epoch;   // [max_requests] episode number
     int32_t* err_cap;           // [max_requests]: epoch of a step past max_steps (nothing written)
+    int32_t* done;              // [max_requests] workgroups of the launch that finished (0 between launches)
     int32_t H, W, T_max, max_requests;
     int32_t write_index;        // 1: this launch writes the next step's ancestry rows and order
     int32_t beams_per_block;    // multiple of kChunk, or >= W
@@ -94,13 +95,6 @@ hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int
 hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
 // Set the launch attributes the step kernel needs for this shape (once, before any launch).
 hipError_t prepare_step(int dk, int dv, int T_max, int W);
-// Graph mode: steps[slot[i]] += 1 (saturating at T_max) after a step launch.
-struct AdvanceParams {
-    int32_t* dev_steps;
-    int32_t T_max, n;
-    int32_t slot[kMaxReqPerLaunch];
-};
-hipError_t launch_advance(const AdvanceParams& a, hipStream_t s);
 // steps[req] = steps_value, epoch[req] = epoch_value (a request restarts).
 hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, int steps_value, int epoch_value,
                                hipStream_t s);

@@ -148,16 +148,52 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     if (p.dev_steps) {                            // graph mode: the counters live on the device
         t = p.dev_steps[slot] + 1;
         epoch = p.dev_epoch[slot];
-        if (t > p.T_max) {                        // no record slot left: report, write nothing
-            if (threadIdx.x == 0) p.err_cap[slot] = epoch;
-            return;
+    }
+    // The previous step's beam order and this step's parents are loaded
+    // first, so that the ordering below overlaps the S0 loads. The order is
+    // read at both step parities: in graph mode the step index is not known
+    // before its counter arrives. (Indices clamped into the arrays; the
+    // values go unused at t = 1.)
+    constexpr int OU = (kOrderMax + NT - 1) / NT;
+    int po0[OU], po1[OU], pa[OU];
+    {
+        const int* order0 = p.order + (size_t)slot * p.W;
+        const int* order1 = p.order + ((size_t)p.max_requests + slot) * p.W;
+        const int* prow = p.parent ? p.parent + (size_t)ri * p.W : order0;
+#pragma unroll
+        for (int u = 0; u < OU; ++u) {
+            const int i = min(tid + u * NT, p.W - 1);
+            po0[u] = order0[i];
+            po1[u] = order1[i];
+            pa[u] = prow[i];
         }
+    }
+    // Graph mode: the last workgroup of a request to finish advances its step
+    // counter. Every wave reads the counter before its first barrier, and
+    // thread 0 counts its workgroup only after the last one, so no workgroup
+    // of the launch can see the advanced value.
+    auto count_done = [&]() __attribute__((always_inline)) {
+        if (p.dev_steps && threadIdx.x == 0) {
+            const int before = atomicAdd(&p.done[slot], 1);
+            if (before == p.H * p.n_splits - 1) {
+                p.done[slot] = 0;
+                if (t <= p.T_max) p.dev_steps[slot] = t;
+            }
+        }
+    };
+    if (t > p.T_max) {                            // (graph mode) no record slot left: report, write nothing
+        if (threadIdx.x == 0) p.err_cap[slot] = epoch;
+        count_done();
+        return;
     }
     const int H = p.H, W = p.W;
     const int depth = t - 1;                      // ancestral records per beam
     const int b_begin = split * p.beams_per_block;
     const int b_end = min(W, b_begin + p.beams_per_block);
-    if (b_begin >= b_end) return;
+    if (b_begin >= b_end) {
+        count_done();
+        return;
+    }
 
     // Uniform 64-bit bases of this (request, head); every per-lane offset from
     // them is a 32-bit int (the host rejects shapes where that could overflow).
@@ -178,23 +214,9 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     uint16_t* rkey = p.rec_k + rec0 * DK;                          // record r: rkey + r*DK
     const int* anc_prev = p.anc + ((size_t)((t - 1) & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* anc_next = p.anc + ((size_t)(t & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
-    const int* ord_prev = p.order + ((size_t)((t - 1) & 1) * p.max_requests + slot) * W;
     int* ord_next = p.order + ((size_t)(t & 1) * p.max_requests + slot) * W;
 
-    // The previous order and this step's parents are loaded before S0, so
-    // the ordering below runs while the S0 fragments are in flight (indices
-    // clamped into the arrays; at t = 1 there is no parent to order by).
     const bool ordered = W <= kOrderMax;
-    constexpr int OU = (kOrderMax + NT - 1) / NT;
-    int po[OU] = {}, pa[OU] = {};
-    if (depth > 0) {
-#pragma unroll
-        for (int u = 0; u < OU; ++u) {
-            const int i = min(tid + u * NT, W - 1);
-            po[u] = ord_prev[i];
-            pa[u] = parin[i];
-        }
-    }
     __builtin_amdgcn_sched_barrier(0);
 
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
@@ -223,7 +245,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
 #pragma unroll
             for (int u = 0; u < OU; ++u) {
                 const int i = tid + u * NT;
-                if (i < W) pos_s[min((unsigned)po[u], (unsigned)(W - 1))] = i;   // position of each step t-1 beam
+                const int po = (depth & 1) ? po1[u] : po0[u];                 // order of step t-1
+                if (i < W) pos_s[min((unsigned)po, (unsigned)(W - 1))] = i;   // position of each step t-1 beam
             }
             lds_barrier();
 #pragma unroll
@@ -537,6 +560,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             anc_next[b * p.T_max + depth - 1] = (depth - 1) * W + pb;
         }
     }
+    count_done();
 }
 
 template <int DK, int DV>
@@ -560,14 +584,6 @@ hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
     const int nblk = p.n_req * p.H * p.n_splits;
     hipLaunchKernelGGL((step_kernel<DK, DV>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
     return hipGetLastError();
-}
-
-__global__ __launch_bounds__(64) void advance_kernel(const AdvanceParams a) {
-    const int i = threadIdx.x;
-    if (i < a.n) {
-        const int c = a.dev_steps[a.slot[i]];
-        a.dev_steps[a.slot[i]] = c < a.T_max ? c + 1 : c;
-    }
 }
 
 __global__ __launch_bounds__(64) void set_counters_kernel(int32_t* steps, int32_t* epoch, int req, int sv, int ev) {
@@ -605,11 +621,6 @@ hipError_t prepare_step(int dk, int dv, int T_max, int W) {
     if (dk == 64 && dv == 64) return prepare_step_t<64, 64>(T_max, W);
     if (dk == 128 && dv == 128) return prepare_step_t<128, 128>(T_max, W);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_advance(const AdvanceParams& a, hipStream_t s) {
-    hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, a);
-    return hipGetLastError();
 }
 
 hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, int steps_value, int epoch_value,

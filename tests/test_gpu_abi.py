@@ -153,5 +153,5 @@ def test_memory_accounting():
     m = lay.memory()
     assert m["s0_bytes"] == shape.H * 128 * 128 * 4
     assert m["record_bytes"] == shape.H * shape.T * shape.W * (4 + 4 * 128 + 2 * 128)
-    assert m["index_bytes"] == 2 * shape.W * shape.T * 4 + 2 * shape.W * 4 + 4 * 4   # + 4 words per request
+    assert m["index_bytes"] == 2 * shape.W * shape.T * 4 + 2 * shape.W * 4 + 5 * 4   # + 5 words per request
     lay.close()

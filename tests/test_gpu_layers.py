@@ -69,7 +69,7 @@ def test_shared_index_layers_equal_independent_layers():
             assert np.array_equal(lay.get_ancestry(i), ref["anc"][-1][i])
         ref["layer"].close()
     mem = [lay.memory() for lay in layers]
-    assert mem[1]["index_bytes"] == 16 * n and mem[2]["index_bytes"] == 16 * n   # per-request words only
+    assert mem[1]["index_bytes"] == 20 * n and mem[2]["index_bytes"] == 20 * n   # per-request words only
     _close(layers)
 
 
