@@ -74,6 +74,19 @@ def test_parity_ragged_beams(W, T, H, d):
     outs["layer"].close()
 
 
+@pytest.mark.parametrize("W,T,H,d", [(40, 12, 2, 64), (16, 20, 1, 128), (8, 64, 1, 32)])
+def test_parity_deep_histories(W, T, H, d):
+    """Histories longer than the short decode horizons of the pages' workload,
+    up to the 64-step maximum: many older blocks of delta gathers per beam,
+    long ancestry rows, and (at 64 steps) the largest LDS footprint."""
+    shape = shape_of(0, name=f"deep_t{T}", H=H, dk=d, dv=d, W=W, T=T, R=2)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] deep history W={W} T={T} H={H} d={d}", flush=True)
+    outs = gh.run_episode(shape, ep, S0)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(2) for h in range(H)])
+    outs["layer"].close()
+
+
 def test_tile_size_invariance_and_determinism():
     """Outputs are bit-identical across launch shapes and across runs."""
     shape = shape_of(1, R=2, T=4)
