@@ -12,12 +12,14 @@ pointers directly. The method's projection replay is written out separately
 Pins (tests/test_oracle_pins.py): a hand-worked scalar example, the identity
 and pure-decay closed forms along parent paths, the delta-rule product form,
 the write-back property, exact associative recall with orthonormal keys,
-affinity in S0, beam-relabelling equivariance, replay == full state, and a
-brute-force ancestry walk. No function here is "parity unpinned".
+affinity in S0, beam-relabelling equivariance, replay == full state, a
+brute-force ancestry walk, and closed forms of the input-side gates and
+normalisation (`fused_inputs`). No function here is "parity unpinned".
 """
 from .gdn import (  # noqa: F401
     ancestry_walk,
     full_state_episode,
+    fused_inputs,
     prompt_state,
     replay_episode,
 )

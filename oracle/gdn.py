@@ -180,3 +180,37 @@ def replay_episode(S0, q, k, v, alpha, beta, parents):
         rec_d[ids] = delta[i]
         rec_k[ids] = k[i]
     return {"o": o, "delta": delta}
+
+
+# ------------------------------------------------------ input-side fusion
+# The pages do not describe how a layer forms q, k, alpha and beta from its
+# projections. The reading used here is the usual gated DeltaNet layer: q and
+# k are L2-normalised per head, alpha = exp(-exp(A_log) * softplus(a + dt_bias))
+# with per-head parameters A_log and dt_bias, and beta = sigmoid(b).
+
+def _bf16_round(x32) -> np.ndarray:
+    """float32 values rounded to the nearest bf16 (ties to even), as float32."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def fused_inputs(q_raw, k_raw, a_raw, b_raw, A_log, dt_bias, eps=1e-6):
+    """Decode-step inputs from raw projections.
+
+    q_raw, k_raw: [..., H, d] float values; a_raw, b_raw: [..., H];
+    A_log, dt_bias: [H]. Returns (q, k, alpha, beta): q and k divided by
+    sqrt(sum of squares + eps) per head in float32 and rounded to bf16 (the
+    precision the step consumes them in, so both sides take that rounding
+    decision in the same precision), alpha and beta in float64.
+    """
+    def unit(x):
+        x = np.asarray(x, dtype=np.float32)
+        s = np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32) + np.float32(eps)
+        return _bf16_round(x / np.sqrt(s))
+
+    a = _f64(a_raw) + _f64(dt_bias)
+    softplus = np.where(a > 20.0, a, np.log1p(np.exp(np.minimum(a, 20.0))))
+    alpha = np.exp(-np.exp(_f64(A_log)) * softplus)
+    beta = 1.0 / (1.0 + np.exp(-_f64(b_raw)))
+    return unit(q_raw), unit(k_raw), alpha, beta

@@ -12,7 +12,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import ancestry_walk, full_state_episode, prompt_state, replay_episode
+from oracle import ancestry_walk, full_state_episode, fused_inputs, prompt_state, replay_episode
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -226,3 +226,46 @@ def test_out_of_range_parent_rejected():
     par[1, 0] = 3
     with pytest.raises(ValueError):
         full_state_episode(S0, q, k, v, alpha, beta, par)
+
+
+# ------------------------------------------------------ input-side fusion
+def test_fused_gates_closed_forms():
+    """alpha = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b) at
+    points where they have exact values: softplus(0) = ln 2 gives
+    alpha = 2^-exp(A_log); a very negative argument leaves no decay; a large
+    one decays by exp(-A (a + dt_bias)); sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4."""
+    H = 4
+    A_log = np.array([0.0, np.log(3.0), np.log(0.5), 0.0])
+    dt_bias = np.array([-2.0, 1.5, 0.25, -3.0])
+    a_raw = np.array([[2.0, -1.5, -0.25, -60.0]])      # a + dt_bias = 0, 0, 0, -63
+    b_raw = np.array([[0.0, np.log(3.0), -np.log(3.0), 0.0]])
+    _, _, alpha, beta = fused_inputs(np.ones((1, H, 8)), np.ones((1, H, 8)), a_raw, b_raw, A_log, dt_bias)
+    np.testing.assert_allclose(alpha[0, :3], [0.5, 0.125, 2 ** -0.5], rtol=1e-15)
+    assert abs(alpha[0, 3] - 1.0) < 1e-20
+    np.testing.assert_allclose(beta[0], [0.5, 0.75, 0.25, 0.5], rtol=1e-15)
+    _, _, alpha, _ = fused_inputs(np.ones((1, 1, 8)), np.ones((1, 1, 8)), np.array([[30.0]]), np.zeros((1, 1)),
+                                  np.array([np.log(2.0)]), np.array([0.5]))
+    np.testing.assert_allclose(alpha[0, 0], np.exp(-2.0 * 30.5), rtol=1e-14)
+
+
+def test_fused_normalisation():
+    """Per-head L2 normalisation rounded to bf16: (3, 4, 0, ...) becomes the
+    bf16 neighbours of (0.6, 0.8); power-of-two scaling of the raw vector
+    changes nothing (eps = 0); every normalised vector has unit length to
+    within bf16 rounding; heads are normalised independently."""
+    x = np.zeros((1, 2, 32))
+    x[0, 0, :2] = [3.0, 4.0]
+    x[0, 1, 5] = -7.0
+    q, _, _, _ = fused_inputs(x, x, np.zeros((1, 2)), np.zeros((1, 2)), np.zeros(2), np.zeros(2))
+    assert q[0, 0, 0] == np.float32(0.6015625) and q[0, 0, 1] == np.float32(0.80078125)
+    assert np.count_nonzero(q[0, 0]) == 2 and q[0, 1, 5] == -1.0 and np.count_nonzero(q[0, 1]) == 1
+    rng = np.random.default_rng(5)
+    raw = rng.standard_normal((50, 3, 64)).astype(np.float32)
+    base, k1, _, _ = fused_inputs(raw, raw, np.zeros((50, 3)), np.zeros((50, 3)), np.zeros(3), np.zeros(3), eps=0.0)
+    for scale in (2.0 ** -7, 2.0 ** 9):
+        scaled, _, _, _ = fused_inputs(raw * np.float32(scale), raw, np.zeros((50, 3)), np.zeros((50, 3)),
+                                       np.zeros(3), np.zeros(3), eps=0.0)
+        assert np.array_equal(scaled, base)
+    norms = np.linalg.norm(base.astype(np.float64), axis=-1)
+    assert np.all(np.abs(norms - 1.0) <= 2.0 ** -8)
+    assert np.array_equal(base, k1)

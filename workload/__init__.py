@@ -10,7 +10,9 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     decode_inputs,
     f32_to_bf16_bits,
+    gate_params,
     make_episode,
+    make_raw_episode,
     prompt_tokens,
     shape_of,
 )

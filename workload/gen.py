@@ -28,6 +28,8 @@ STREAM_S0 = 0
 STREAM_PROMPT = 1
 STREAM_DECODE = 2
 STREAM_PARENTS = 3
+STREAM_RAW = 4         # raw projections of the decode step (input-side fusion)
+STREAM_GATES = 5       # per-head gate parameters
 
 
 @dataclass(frozen=True)
@@ -153,6 +155,45 @@ def parents_for(shape: Shape, req: int) -> np.ndarray:
     else:
         raise ValueError(f"unknown parent rule {shape.parents!r}")
     return par
+
+
+def raw_decode_inputs(shape: Shape, req: int) -> dict:
+    """Raw projections of one request for all T steps (input-side fusion).
+
+    q_raw, k_raw [T][W][H][dk] uint16 bf16 bits of N(0, 1) draws (not
+    normalised); v [T][W][H][dv] as in `decode_inputs`; a_raw, b_raw
+    [T][W][H] float32 ~ N(0, 1).
+    """
+    rng = _rng(shape.cfg, req, STREAM_RAW)
+    T, W, H = shape.T, shape.W, shape.H
+    q = f32_to_bf16_bits(rng.standard_normal((T, W, H, shape.dk)).astype(np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((T, W, H, shape.dk)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((T, W, H, shape.dv)).astype(np.float32))
+    a = rng.standard_normal((T, W, H)).astype(np.float32)
+    b = rng.standard_normal((T, W, H)).astype(np.float32)
+    return {"q_raw": q, "k_raw": k, "v": v, "a_raw": a, "b_raw": b}
+
+
+def gate_params(shape: Shape) -> dict:
+    """Per-head gate parameters: A_log ~ U[0, ln 16], dt_bias ~ U[-6.9, -2.3]
+    (the range that puts a layer's decay near 0.45-0.95 for N(0, 1) inputs)."""
+    rng = _rng(shape.cfg, 0, STREAM_GATES)
+    return {"A_log": rng.uniform(0.0, np.log(16.0), shape.H).astype(np.float32),
+            "dt_bias": rng.uniform(-6.9, -2.3, shape.H).astype(np.float32)}
+
+
+def make_raw_episode(shape: Shape, reqs=None) -> dict:
+    """Like `make_episode` with raw projections instead of q, k, alpha, beta:
+    q_raw, k_raw, v, a_raw, b_raw stacked over requests, parents [T][n][W],
+    S0 [n][H][dv][dk] (drawn), and the per-head A_log, dt_bias [H]."""
+    reqs = list(range(shape.R)) if reqs is None else list(reqs)
+    parts = [raw_decode_inputs(shape, r) for r in reqs]
+    out = {key: np.concatenate([p[key] for p in parts], axis=1) for key in parts[0]}
+    out["parents"] = np.stack([parents_for(shape, r) for r in reqs], axis=1)
+    out["S0"] = np.stack([s0_normal(shape, r) for r in reqs], axis=0)
+    out.update(gate_params(shape))
+    out["reqs"] = reqs
+    return out
 
 
 def make_episode(shape: Shape, reqs=None, with_s0: bool = True) -> dict:
