@@ -190,6 +190,57 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     }
 
 
+def fused_leg(shape, ep, q, k, v, al, be, par, S0, bytes_t, runs=20):
+    """The same decode steps through onela_step_raw (input-side fusion: q, k
+    normalised, alpha and beta formed from raw projections inside the launch,
+    o written as bf16). Raw inputs of the same shapes stand in for the
+    projections (the cost does not depend on their values). Returns the
+    launch time per depth and the HBM rate of its algorithmic bytes (the
+    decode step's, with o at 2 bytes per element)."""
+    import torch
+
+    from linear_attention_beam_gdn_amd import Onela
+    from workload import gate_params
+
+    R, H, W, T = shape.R, shape.H, shape.W, shape.T
+    stream = torch.cuda.current_stream()
+    lay = Onela(R, H, shape.dk, shape.dv, W, T, stream=stream)
+    for r in range(R):
+        lay.init_request(r, S0[r].contiguous())
+    g = gate_params(shape)
+    A = torch.from_numpy(g["A_log"]).cuda()
+    D = torch.from_numpy(g["dt_bias"]).cuda()
+    o16 = torch.empty((R * W, H, shape.dv), dtype=torch.int16, device=q[0].device)
+    reqs = list(range(R))
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+    per = []
+    for it in range(runs + 2):
+        for r in reqs:
+            lay.reset(r)
+        for t in range(T):
+            ev[t][0].record(stream)
+            lay.step_raw(reqs, q[t], k[t], v[t], al[t], be[t], A, D, par[t], o16)
+            ev[t][1].record(stream)
+        torch.cuda.synchronize()
+        if it >= 2:
+            per.append([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(T)])
+    lay.sync()
+    lay.close()
+    us = np.median(np.array(per), axis=0)
+    nbytes = [b["total"] - R * W * H * 2 * shape.dv for b in bytes_t]     # o at 2 B instead of 4
+    mean_s = float(np.mean(np.array(per))) * 1e-6
+    gbs = float(np.mean(nbytes)) / mean_s / 1e9
+    return {
+        "what": "onela_step_raw: per-head q/k L2 normalisation, alpha = exp(-exp(A_log) softplus(a + dt_bias)), "
+                "beta = sigmoid(b) inside the launch, o as bf16",
+        "kernel": "step_kernel<128, 128, true>",
+        "kernel_us_mean": mean_s * 1e6,
+        "us_by_depth": [round(float(x), 2) for x in us],
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": float(np.mean(nbytes))},
+    }
+
+
 def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
     """A decode step of n_layers GDN layers sharing one ancestry index, eager vs
     one HIP graph per decode step (graph mode: step counters on the device).
@@ -372,6 +423,7 @@ def main():
     ap.add_argument("--s0", choices=("prompt", "normal"), default="prompt",
                     help="S0 folded on the GPU from a synthetic prompt (default) or drawn N(0, 0.05^2)")
     ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
+    ap.add_argument("--no-fused", action="store_true", help="skip the input-side fusion leg")
     ap.add_argument("--layers", type=int, default=4,
                     help="layers of the multi-layer decode-step leg (eager vs HIP graph); 0 skips it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -427,7 +479,7 @@ def main():
     prefill_out = None
     if args.s0 == "prompt":
         S0_dev, prefill_out = prompt_s0(lay, shape, args.prompt_len, reqs, dev, stream,
-                                        need_f32=not args.no_fullstate or args.layers > 0)
+                                        need_f32=not (args.no_fullstate and args.no_fused) or args.layers > 0)
         s0_label = (f"prompt-derived: the GDN recurrence over {args.prompt_len} synthetic tokens per request "
                     "and head, folded on the GPU (prefill_kernel)")
     else:
@@ -520,6 +572,9 @@ def main():
         out["prefill"] = prefill_out
     mem = lay.memory()
     lay.close()
+    if not args.no_fused:
+        out["fused_inputs"] = fused_leg(shape, ep, q, k, v, al, be, par,
+                                        S0_dev if S0_dev is not None else up(ep["S0"]), bytes_t)
     if args.layers > 0:
         S0_ml = S0_dev if S0_dev is not None else up(ep["S0"])
         out["multi_layer"] = multi_layer_leg(shape, args.layers, q, k, v, al, be, par, S0_ml)

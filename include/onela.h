@@ -188,6 +188,32 @@ onela_status onela_reset(onela_ctx* ctx, int32_t req);
  * poisoned by a bad parent index, ONELA_E_HIP on a HIP failure. */
 onela_status onela_sync(onela_ctx* ctx);
 
+/* ---- input-side fusion ----------------------------------------------------
+ * A GDN layer forms q, k, alpha and beta from its projections before the
+ * step. The pages do not describe that part; this entry point takes the usual
+ * gated DeltaNet parametrisation and fuses it into the step launch:
+ *   q = q_raw / sqrt(|q_raw|^2 + norm_eps), k likewise (per head, float32,
+ *     rounded to bf16 before use; the records hold these keys),
+ *   alpha = exp(-exp(A_log[h]) * softplus(a_raw + dt_bias[h])),
+ *   beta  = sigmoid(b_raw),
+ * and writes o as bf16 (nearest, ties to even) for the layer's next matmul.
+ * The records' alpha are the computed alpha. */
+typedef struct {
+    const float* A_log;     /* device float32 [H] */
+    const float* dt_bias;   /* device float32 [H] */
+    float norm_eps;         /* >= 0, added to the sum of squares (e.g. 1e-6) */
+} onela_gate_params;
+
+/* onela_step with raw inputs: q_raw, k_raw device bf16 [n_req*W][H][d_k]
+ * (16-byte aligned), v as in onela_step, a_raw, b_raw device float32
+ * [n_req*W][H], gates (host struct, device arrays), o_bf16 device bf16
+ * [n_req*W][H][d_v] (8-byte aligned). delta_out (float32), parents, request
+ * list, errors and state changes as in onela_step; graph mode applies. */
+onela_status onela_step_raw(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
+                            const uint16_t* q_raw, const uint16_t* k_raw, const uint16_t* v,
+                            const float* a_raw, const float* b_raw, const onela_gate_params* gates,
+                            const int32_t* parent_idx, uint16_t* o_bf16, float* delta_out);
+
 /* Graph mode on (1) or off (0). In graph mode each request's step index and
  * episode number live in device memory and each step launch advances them
  * itself (the last workgroup of a request to finish), so the launches of a

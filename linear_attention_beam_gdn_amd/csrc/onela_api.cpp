@@ -311,14 +311,20 @@ onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams) {
     return ONELA_OK;
 }
 
-onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q,
-                        const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
-                        const int32_t* parent_idx, float* o, float* delta_out) {
-    if (!ctx || n_req < 1 || n_req > ctx->cfg.max_requests || !reqs || !q || !k || !v || !alpha || !beta || !o)
+// One decode step for the listed requests. fused: q, k, alpha, beta are raw
+// projections (gates non-null) and o goes to o16 as bf16; else o is float32.
+static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q,
+                              const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+                              const int32_t* parent_idx, float* o, uint16_t* o16, float* delta_out,
+                              const onela_gate_params* gates) {
+    const bool fused = gates != nullptr;
+    if (!ctx || n_req < 1 || n_req > ctx->cfg.max_requests || !reqs || !q || !k || !v || !alpha || !beta ||
+        (fused ? !o16 : !o))
         return ONELA_E_INVALID_ARG;
-    // vector loads and stores: 16 B for q, k, o, delta_out; 8 B for v; 4 B for the rest
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 8) || !aligned(o, 16) || !aligned(delta_out, 16) ||
-        !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(parent_idx, 4))
+    if (fused && (!gates->A_log || !gates->dt_bias || !(gates->norm_eps >= 0.f))) return ONELA_E_INVALID_ARG;
+    // vector loads and stores: 16 B for q, k, o, delta_out; 8 B for v and bf16 o; 4 B for the rest
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 8) || !aligned(o, 16) || !aligned(o16, 8) ||
+        !aligned(delta_out, 16) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(parent_idx, 4))
         return ONELA_E_INVALID_ARG;
     const auto& c = ctx->cfg;
     std::vector<char> seen(c.max_requests, 0);
@@ -358,6 +364,11 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
     p.dev_epoch = ctx->dev_epoch;
     p.err_cap = ctx->err_cap;
     p.done = ctx->done;
+    if (fused) {
+        p.A_log = gates->A_log;
+        p.dt_bias = gates->dt_bias;
+        p.norm_eps = gates->norm_eps;
+    }
     p.H = c.num_heads;
     p.W = c.beam_width;
     p.T_max = c.max_steps;
@@ -372,7 +383,8 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
         p.alpha = alpha + rows * H;
         p.beta = beta + rows * H;
         p.parent = parent_idx ? parent_idx + rows : nullptr;
-        p.o = o + rows * H * c.d_v;
+        p.o = o ? o + rows * H * c.d_v : nullptr;
+        p.o_bf16 = o16 ? o16 + rows * H * c.d_v : nullptr;
         p.delta_out = delta_out ? delta_out + rows * H * c.d_v : nullptr;
         p.n_req = n;
         p.beams_per_block = ctx->beams_per_block ? ctx->beams_per_block : auto_beams_per_block(ctx, n * c.num_heads);
@@ -382,12 +394,26 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, cons
             p.t[i] = ctx->steps[reqs[i0 + i]] + 1;
             p.epoch[i] = ctx->epoch[reqs[i0 + i]];
         }
-        hipError_t e = onela::launch_step(c.d_k, c.d_v, p, ctx->stream);
+        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
         if (!ctx->graph_mode)                     // (graph mode: the launch advances the device counters)
             for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;
     }
     return ONELA_OK;
+}
+
+onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v, const float* alpha, const float* beta,
+                        const int32_t* parent_idx, float* o, float* delta_out) {
+    return step_impl(ctx, n_req, reqs, q, k, v, alpha, beta, parent_idx, o, nullptr, delta_out, nullptr);
+}
+
+onela_status onela_step_raw(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q_raw,
+                            const uint16_t* k_raw, const uint16_t* v, const float* a_raw, const float* b_raw,
+                            const onela_gate_params* gates, const int32_t* parent_idx, uint16_t* o_bf16,
+                            float* delta_out) {
+    if (!gates) return ONELA_E_INVALID_ARG;
+    return step_impl(ctx, n_req, reqs, q_raw, k_raw, v, a_raw, b_raw, parent_idx, nullptr, o_bf16, delta_out, gates);
 }
 
 onela_status onela_sync(onela_ctx* ctx) {

@@ -39,6 +39,12 @@ struct StepParams {
     int32_t* err_cap;           // [max_requests]: epoch of a step past max_steps (nothing written)
     int32_t* done;              // [max_requests] workgroups of the launch that finished (0 between launches)
     int32_t H, W, T_max, max_requests;
+    // Input-side fusion (the fused kernel variant): q, k, alpha, beta above are
+    // raw projections; o_bf16 receives o instead of o.
+    const float* A_log;         // [H]
+    const float* dt_bias;       // [H]
+    float norm_eps;
+    uint16_t* o_bf16;           // [n_req*W][H][DV] bf16
     int32_t write_index;        // 1: this launch writes the next step's ancestry rows and order
     int32_t beams_per_block;    // multiple of kChunk, or >= W
     int32_t n_splits;           // ceil(W / beams_per_block)
@@ -92,7 +98,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 hipError_t launch_prefill(int dk, int dv, bool planes, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fullstate_step(int dk, int dv, const FullStateParams& p, hipStream_t s);
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
-hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s);
+hipError_t launch_step(int dk, int dv, bool fused, const StepParams& p, hipStream_t s);
 // Set the launch attributes the step kernel needs for this shape (once, before any launch).
 hipError_t prepare_step(int dk, int dv, int T_max, int W);
 // steps[req] = steps_value, epoch[req] = epoch_value (a request restarts).

@@ -96,7 +96,26 @@ __global__ __launch_bounds__(256) void init_s0_kernel(const float* __restrict__ 
 template <int DV>
 __host__ __device__ constexpr int step_threads() { return 64 * (DV / kRowsPerWave); }
 
-template <int DK, int DV>
+// Input-side fusion: a layer's raw gate projections to the step's decay and
+// write strength, alpha = exp(-exp(A_log) softplus(a + dt_bias)) and
+// beta = sigmoid(b) (the usual gated DeltaNet parametrisation; the pages do
+// not describe it).
+__device__ __forceinline__ float gate_alpha(float a_raw, float neg_A, float dt_bias) {
+    const float x = a_raw + dt_bias;
+    const float softplus = x > 20.f ? x : log1pf(expf(x));
+    return expf(neg_A * softplus);
+}
+
+__device__ __forceinline__ float gate_beta(float b_raw) { return 1.f / (1.f + expf(-b_raw)); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// FUSED: q, k arrive as raw projections and are L2-normalised per head in
+// phase A (float32, rounded to bf16 before any use, so records hold the keys
+// the step used); alpha and beta arrive raw; o leaves as bf16.
+template <int DK, int DV, bool FUSED>
 __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
     constexpr int CH = kChunk;
     constexpr int NW = DV / kRowsPerWave;
@@ -206,7 +225,11 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     const uint16_t* vin = p.v + in0 * DV;
     const float* ain = p.alpha + in0;
     const float* bin = p.beta + in0;
-    float* oout = p.o + in0 * DV;
+    float* oout = FUSED ? nullptr : p.o + in0 * DV;
+    uint16_t* oout16 = FUSED ? p.o_bf16 + in0 * DV : nullptr;
+    // (uniform values, kept in scalar registers)
+    const float neg_A = FUSED ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(-expf(p.A_log[h])))) : 0.f;
+    const float dtb = FUSED ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.dt_bias[h]))) : 0.f;
     float* dout = p.delta_out ? p.delta_out + in0 * DV : nullptr;
     const int* parin = depth > 0 ? p.parent + (size_t)ri * W : nullptr;
     float* ralpha = p.rec_alpha + rec0;                            // record r: ralpha[r]
@@ -356,6 +379,26 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             for (int j = 0; j + 1 < depth; ++j) anc_s[j * CH + tid_l] = src[j];
             anc_s[(depth - 1) * CH + tid_l] = (depth - 1) * W + par;   // parent's own record of step t-1
         }
+        if constexpr (FUSED) {
+            // a row's SEG pieces sit in SEG adjacent lanes of one wave
+            static_assert((2 * CH * SEG) % NT == 0 && 64 % SEG == 0, "whole rows per wave");
+#pragma unroll
+            for (int it = 0; it < XITER; ++it) {
+                float x[8], ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[2 * e] = bf_lo(xv[it][e]);
+                    x[2 * e + 1] = bf_hi(xv[it][e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+                for (int m = 1; m < SEG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float inv = 1.f / sqrtf(ss + p.norm_eps);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[it][e] = pack_bf16x2(x[2 * e] * inv, x[2 * e + 1] * inv);
+            }
+        }
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
             const int idx = tid_l + it * NT;
@@ -373,8 +416,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             }
         }
         if (beam_thread) {
-            at_s[tid_l] = a_new;
-            bt_s[tid_l] = b_new;
+            at_s[tid_l] = FUSED ? gate_alpha(a_new, neg_A, dtb) : a_new;
+            bt_s[tid_l] = FUSED ? gate_beta(b_new) : b_new;
         }
         lds_barrier();
 
@@ -530,7 +573,11 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 o.y = fmaf(a, yq[1], kq * d.y);
                 o.z = fmaf(a, yq[2], kq * d.z);
                 o.w = fmaf(a, yq[3], kq * d.w);
-                *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
+                if constexpr (FUSED)
+                    *reinterpret_cast<uint2*>(oout16 + b * HV + rbase) =
+                        make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+                else
+                    *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
                 *reinterpret_cast<float4*>(rdelta + (depth * W + b) * DV + rbase) = d;
                 if (dout) *reinterpret_cast<float4*>(dout + b * HV + rbase) = d;
             }
@@ -552,7 +599,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // order over this workgroup's index range (the splits of a (request,
     // head) cover [0, W) between them), so the small writes coalesce.
     for (int b = b_begin + tid; b < b_end; b += NT) {
-        ralpha[depth * W + b] = ain[b * H];
+        ralpha[depth * W + b] = FUSED ? gate_alpha(ain[b * H], neg_A, dtb) : ain[b * H];
         if (p.write_index && h == 0 && depth > 0) {   // one head of the index owner writes it
             int pb = parin[b];
             pb = (pb < 0 || pb >= W) ? 0 : pb;         // (reported in phase A)
@@ -574,15 +621,21 @@ template <int DK, int DV>
 hipError_t prepare_step_t(int T_max, int W) {
     const size_t lds = step_lds_bytes(DK, DV, T_max, W);
     if (lds <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV, true>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 template <int DK, int DV>
-hipError_t launch_step_t(const StepParams& p, hipStream_t s) {
+hipError_t launch_step_t(bool fused, const StepParams& p, hipStream_t s) {
     const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
     const int nblk = p.n_req * p.H * p.n_splits;
-    hipLaunchKernelGGL((step_kernel<DK, DV>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
+    if (fused)
+        hipLaunchKernelGGL((step_kernel<DK, DV, true>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
+    else
+        hipLaunchKernelGGL((step_kernel<DK, DV, false>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
     return hipGetLastError();
 }
 
@@ -630,10 +683,10 @@ hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, 
     return hipGetLastError();
 }
 
-hipError_t launch_step(int dk, int dv, const StepParams& p, hipStream_t s) {
-    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(p, s);
-    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(p, s);
-    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(p, s);
+hipError_t launch_step(int dk, int dv, bool fused, const StepParams& p, hipStream_t s) {
+    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, p, s);
+    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, p, s);
+    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -30,7 +30,7 @@ EXPORTED = (
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
     "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
-    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode",
+    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode", "onela_step_raw",
 )
 
 
@@ -44,6 +44,10 @@ class OnelaError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("max_requests", "num_heads", "d_k", "d_v", "beam_width", "max_steps")]
+
+
+class _Gates(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -83,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_prefill": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
         "onela_create_sharing_index": (i32, [ctypes.POINTER(_Config), vp, vp, ctypes.POINTER(vp)]),
         "onela_set_graph_mode": (i32, [vp, i32]),
+        "onela_step_raw": (i32, [vp, i32, p_i32, vp, vp, vp, vp, vp, ctypes.POINTER(_Gates), vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -197,6 +202,32 @@ class Onela:
             _ptr(delta_out, "delta_out", f32, (rows, c.num_heads, c.d_v), optional=True),
         )
         self._check(st, "onela_step")
+
+    def step_raw(self, reqs, q_raw, k_raw, v, a_raw, b_raw, A_log, dt_bias, parent_idx, o_bf16, delta_out=None,
+                 norm_eps=1e-6):
+        """onela_step from raw projections (q, k normalised, gates computed in the launch), o in bf16."""
+        torch = self._torch
+        c = self.cfg
+        n = len(reqs)
+        rows = n * c.beam_width
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        f32 = (torch.float32,)
+        arr = (ctypes.c_int32 * n)(*[int(r) for r in reqs])
+        gates = _Gates(_ptr(A_log, "A_log", f32, (c.num_heads,)), _ptr(dt_bias, "dt_bias", f32, (c.num_heads,)),
+                       float(norm_eps))
+        st = self.lib.onela_step_raw(
+            self._ctx, n, arr,
+            _ptr(q_raw, "q_raw", bf, (rows, c.num_heads, c.d_k)),
+            _ptr(k_raw, "k_raw", bf, (rows, c.num_heads, c.d_k)),
+            _ptr(v, "v", bf, (rows, c.num_heads, c.d_v)),
+            _ptr(a_raw, "a_raw", f32, (rows, c.num_heads)),
+            _ptr(b_raw, "b_raw", f32, (rows, c.num_heads)),
+            ctypes.byref(gates),
+            _ptr(parent_idx, "parent_idx", (torch.int32,), (n, c.beam_width), optional=True),
+            _ptr(o_bf16, "o_bf16", bf, (rows, c.num_heads, c.d_v)),
+            _ptr(delta_out, "delta_out", f32, (rows, c.num_heads, c.d_v), optional=True),
+        )
+        self._check(st, "onela_step_raw")
 
     def reset(self, req: int):
         self._check(self.lib.onela_reset(self._ctx, req), "onela_reset")

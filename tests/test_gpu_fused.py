@@ -1,0 +1,116 @@
+"""Input-side fusion through the C ABI: raw projections in, bf16 o out.
+
+The oracle forms q, k, alpha, beta from the same raw projections
+(`oracle.fused_inputs`) and runs the float64 decode step. Bars:
+* o (bf16): |o - o_ref| <= 1e-3 + 2^-8 |o_ref| (the step's 1e-3 plus the
+  bf16 rounding of o, at most half a unit in the last place, 2^-9 relative);
+* delta (float32): 1e-3;
+* keys in the records: the oracle normalises in float32 and rounds to bf16 as
+  the kernel does, but the sums of squares are added in a different order, so
+  a key element may land on the neighbouring bf16 value: at most one unit in
+  the last place, in at most 1% of the elements;
+* alpha in the records: 1e-5 relative (float32 exp/log1p against float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+if torch.cuda.is_available():
+    import gpu_harness as gh
+    from linear_attention_beam_gdn_amd import Onela, OnelaError
+    from oracle import full_state_episode, fused_inputs
+    from workload import bf16_bits_to_f32, make_raw_episode, shape_of
+
+
+def _run_raw(shape, ep):
+    n, W, H = len(ep["reqs"]), shape.W, shape.H
+    lay = Onela(n, H, shape.dk, shape.dv, W, shape.T)
+    for i in range(n):
+        lay.init_request(i, gh.to_dev(ep["S0"][i]))
+    A, D = gh.to_dev(ep["A_log"]), gh.to_dev(ep["dt_bias"])
+    o16 = torch.empty((n * W, H, shape.dv), dtype=torch.int16, device=gh.dev())
+    d = torch.empty((n * W, H, shape.dv), dtype=torch.float32, device=gh.dev())
+    outs = {"o": [], "delta": []}
+    for t in range(shape.T):
+        par = gh.to_dev(ep["parents"][t].astype(np.int32)) if t else None
+        lay.step_raw(list(range(n)), *[gh.to_dev(ep[key][t]) for key in ("q_raw", "k_raw", "v", "a_raw", "b_raw")],
+                     A, D, par, o16, d, norm_eps=EPS)
+        lay.sync()
+        outs["o"].append(bf16_bits_to_f32(o16.cpu().numpy().view(np.uint16)))
+        outs["delta"].append(d.cpu().numpy().copy())
+    outs["layer"] = lay
+    return outs
+
+
+def _oracle(shape, ep, i, h):
+    sl = slice(i * shape.W, (i + 1) * shape.W)
+    hs = slice(h, h + 1)
+    q, k, a, b = fused_inputs(bf16_bits_to_f32(ep["q_raw"][:, sl, hs]), bf16_bits_to_f32(ep["k_raw"][:, sl, hs]),
+                              ep["a_raw"][:, sl, hs], ep["b_raw"][:, sl, hs], ep["A_log"][hs], ep["dt_bias"][hs],
+                              eps=EPS)
+    ref = full_state_episode(ep["S0"][i, h], q[:, :, 0], k[:, :, 0], bf16_bits_to_f32(ep["v"][:, sl, h]),
+                             a[:, :, 0], b[:, :, 0], ep["parents"][:, i, :])
+    return ref, k[:, :, 0], a[:, :, 0]
+
+
+def _check(shape, ep, outs, pairs):
+    W, T = shape.W, shape.T
+    for i, h in pairs:
+        ref, kn, an = _oracle(shape, ep, i, h)
+        for t in range(T):
+            o = outs["o"][t][i * W:(i + 1) * W, h]
+            assert np.all(np.abs(o - ref["o"][t]) <= 1e-3 + 2.0 ** -8 * np.abs(ref["o"][t])), (i, h, t)
+            assert np.abs(outs["delta"][t][i * W:(i + 1) * W, h] - ref["delta"][t]).max() <= 1e-3, (i, h, t)
+        a_rec, _, k_rec = outs["layer"].get_records(i, h, T * W)
+        k_gpu = bf16_bits_to_f32(k_rec).reshape(T, W, -1)
+        diff = k_gpu != kn
+        assert diff.mean() <= 0.01, (i, h, diff.mean())
+        assert np.all(np.abs(k_gpu - kn) <= 2.0 ** -7 * np.abs(kn) + 1e-30), (i, h)
+        np.testing.assert_allclose(a_rec.reshape(T, W), an, rtol=1e-5)
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (0, {}),
+    (1, {"R": 2, "H": 3, "T": 3}),
+    (0, {"name": "fused_ragged", "W": 65, "T": 4, "H": 2, "dk": 64, "dv": 64, "R": 2}),
+])
+def test_fused_matches_oracle(cfg, over):
+    shape = shape_of(cfg, **over)
+    ep = make_raw_episode(shape)
+    print(f"[fused] {shape.name} W={shape.W} T={shape.T} H={shape.H} d={shape.dk}", flush=True)
+    outs = _run_raw(shape, ep)
+    _check(shape, ep, outs, [(i, h) for i in range(len(ep["reqs"])) for h in range(shape.H)])
+    outs["layer"].close()
+
+
+def test_fused_bench_size_sampled():
+    """The 32-request, W = 256, d = 128 workload from raw projections, at full
+    size in the bench's launch configuration; three sampled (request, head)
+    pairs against the oracle."""
+    shape = shape_of(3)
+    ep = make_raw_episode(shape)
+    print(f"[fused] {shape.name}", flush=True)
+    outs = _run_raw(shape, ep)
+    _check(shape, ep, outs, [(0, 0), (13, 7), (31, 15)])
+    outs["layer"].close()
+
+
+def test_fused_argument_errors():
+    shape = shape_of(0)
+    ep = make_raw_episode(shape)
+    lay = Onela(1, shape.H, 32, 32, shape.W, shape.T)
+    lay.init_request(0, gh.to_dev(ep["S0"][0]))
+    ins = [gh.to_dev(ep[key][0]) for key in ("q_raw", "k_raw", "v", "a_raw", "b_raw")]
+    o16 = torch.empty((shape.W, shape.H, 32), dtype=torch.int16, device=gh.dev())
+    A, D = gh.to_dev(ep["A_log"]), gh.to_dev(ep["dt_bias"])
+    with pytest.raises(OnelaError) as e:
+        lay.step_raw([0], *ins, A, D, None, o16, norm_eps=-1.0)     # negative epsilon
+    assert e.value.status == -1
+    lay.step_raw([0], *ins, A, D, None, o16)
+    lay.sync()
+    assert lay.get_step(0) == 1
+    lay.close()
