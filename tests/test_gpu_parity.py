@@ -87,6 +87,18 @@ def test_parity_deep_histories(W, T, H, d):
     outs["layer"].close()
 
 
+@pytest.mark.parametrize("W,bpb", [(1100, 0), (1300, 256)])
+def test_parity_wide_beam_sets(W, bpb):
+    """Beam sets wider than the ancestry-ordered limit (1024) are processed in
+    index order; ragged last chunk, several workgroups per (request, head)."""
+    shape = shape_of(0, name=f"wide_w{W}", H=2, dk=32, dv=32, W=W, T=3, R=2)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] wide beam set W={W} beams_per_block={bpb}", flush=True)
+    outs = gh.run_episode(shape, ep, S0, beams_per_block=bpb)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(2) for h in range(2)])
+    outs["layer"].close()
+
+
 def test_tile_size_invariance_and_determinism():
     """Outputs are bit-identical across launch shapes and across runs."""
     shape = shape_of(1, R=2, T=4)

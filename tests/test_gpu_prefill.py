@@ -120,6 +120,31 @@ def test_prefill_bench_size_sampled():
         assert err <= S_TOL
 
 
+def test_prompt_init_more_requests_than_one_launch():
+    """70 requests (more than one launch carries) folded into the planes; each
+    equals the float32 fold of its own prompt put through onela_init_request."""
+    shape = shape_of(0, name="prompt_many", H=2, dk=32, dv=32, W=8, T=2, R=70)
+    toks = prompt_tokens_device(shape, gh.dev(), length=20)
+    args = [toks[key] for key in ("k", "v", "alpha", "beta")]
+    S = prefill(*args)
+    a = Onela(70, 2, 32, 32, 8, 2)
+    b = Onela(70, 2, 32, 32, 8, 2)
+    a.init_requests_from_prompts(list(range(70)), *args)
+    for r in range(70):
+        b.init_request(r, S[r].contiguous())
+    ep, _ = gh.episode(shape_of(0, name="prompt_many", H=2, dk=32, dv=32, W=8, T=2, R=70))
+    o_a = torch.empty((70 * 8, 2, 32), dtype=torch.float32, device=gh.dev())
+    o_b = torch.empty_like(o_a)
+    for t in range(2):
+        par = gh.to_dev(ep["parents"][t].astype(np.int32)) if t else None
+        ins = [gh.to_dev(ep[key][t]) for key in ("q", "k", "v", "alpha", "beta")]
+        a.step(list(range(70)), *ins, par, o_a)
+        b.step(list(range(70)), *ins, par, o_b)
+        assert torch.equal(o_a, o_b)
+    a.close()
+    b.close()
+
+
 def test_prefill_bad_arguments():
     shape = shape_of(0, name="prefill_bad", H=2, dk=32, dv=32)
     tok = _host_tokens(shape, 1, 8)
