@@ -212,18 +212,19 @@ def fused_leg(shape, ep, q, k, v, al, be, par, S0, bytes_t, runs=20):
     D = torch.from_numpy(g["dt_bias"]).cuda()
     o16 = torch.empty((R * W, H, shape.dv), dtype=torch.int16, device=q[0].device)
     reqs = list(range(R))
-    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
-    per = []
+    # no synchronisation inside the timed loop: the queue stays ahead of the
+    # GPU, so the events bracket the launches and not the host's enqueueing
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+          for _ in range(runs + 2)]
     for it in range(runs + 2):
         for r in reqs:
             lay.reset(r)
         for t in range(T):
-            ev[t][0].record(stream)
+            ev[it][t][0].record(stream)
             lay.step_raw(reqs, q[t], k[t], v[t], al[t], be[t], A, D, par[t], o16)
-            ev[t][1].record(stream)
-        torch.cuda.synchronize()
-        if it >= 2:
-            per.append([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(T)])
+            ev[it][t][1].record(stream)
+    torch.cuda.synchronize()
+    per = [[ev[it][t][0].elapsed_time(ev[it][t][1]) * 1e3 for t in range(T)] for it in range(2, runs + 2)]
     lay.sync()
     lay.close()
     us = np.median(np.array(per), axis=0)
@@ -268,19 +269,19 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
             lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t] if t else par[1], o)
 
     def run(replay):
-        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
-        per = []
+        # no synchronisation inside the timed loop (the queue stays ahead of the GPU)
+        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+              for _ in range(episodes + 2)]
         for it in range(episodes + 2):
             for lay in layers:
                 for r in reqs:
                     lay.reset(r)
             for t in range(T):
-                ev[t][0].record(s)
+                ev[it][t][0].record(s)
                 replay(t)
-                ev[t][1].record(s)
-            s.synchronize()
-            if it >= 2:
-                per.append([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(T)])
+                ev[it][t][1].record(s)
+        s.synchronize()
+        per = [[ev[it][t][0].elapsed_time(ev[it][t][1]) * 1e3 for t in range(T)] for it in range(2, episodes + 2)]
         for lay in layers:
             lay.sync()
         return np.median(np.array(per), axis=0)
