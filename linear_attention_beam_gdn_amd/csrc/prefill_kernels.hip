@@ -6,10 +6,12 @@
 // prompt tokens s = 1..L of one (sequence, head):
 //   u = S k_s,  delta = beta_s (v_s - alpha_s u),  S <- alpha_s S + delta k_s^T.
 // One workgroup per (sequence, head) keeps S in registers for the whole
-// prompt: two threads per row of S, d_k/2 columns each. Tokens are staged in
+// prompt: each lane holds a quarter of the columns of two rows. Tokens are staged in
 // LDS (as float32) kTokBlock at a time; the next block's loads are in flight
-// while the current block is folded. The result is written either as float32
-// [H][d_v][d_k] or directly as the step kernel's two bf16 planes.
+// while the current block is folded. Within a block S is held as S / c with
+// c the block's running decay, so a token costs two multiply-adds per state
+// element. The result is written either as float32 [H][d_v][d_k] or directly
+// as the step kernel's two bf16 planes.
 #include "onela_internal.h"
 
 namespace onela {
@@ -23,34 +25,39 @@ __host__ __device__ constexpr int prefill_threads() { return 2 * DV; }
 template <int DK, int DV, bool PLANES>
 __global__ __launch_bounds__(prefill_threads<DV>()) void prefill_kernel(const PrefillParams p) {
     constexpr int NT = prefill_threads<DV>();
-    constexpr int C = DK / 2;            // state columns per thread
+    constexpr int C = DK / 4;            // state columns per thread (a quarter of each of its two rows)
     constexpr int TB = kTokBlock;
     constexpr int KP = DK / 8, VP = DV / 8;   // 16-byte pieces per token row
-    // one k piece and one v piece of a block per thread
-    static_assert(TB * KP == NT && TB * VP == NT && C % 8 == 0, "prefill block shape");
+    // one k piece and one v piece of a block per thread; four lanes per row pair
+    static_assert(TB * KP == NT && TB * VP == NT && C % 8 == 0 && NT == 2 * DV, "prefill block shape");
 
     __shared__ __align__(16) float ks[2][TB][DK];
     __shared__ __align__(16) float vsh[2][TB][DV];
     __shared__ float as[2][TB], bs[2][TB];
 
     const int tid = threadIdx.x;
-    const int row = tid >> 1, half = tid & 1;
+    // rows r, r + DV/2 (r = tid / 4), columns [cq*C, cq*C + C) with cq = tid % 4
+    const int cq = tid & 3;
+    const int rows[2] = {tid >> 2, (tid >> 2) + DV / 2};
     const int seq = blockIdx.x / p.H, h = blockIdx.x % p.H;
     const int H = p.H, L = p.L;
     const size_t tok0 = (size_t)seq * L;                 // token 0 of this sequence
     const size_t state0 = ((size_t)seq * H + h) * DV * DK;
 
-    float S[C];
-    if (p.s_init) {
-        const float4* src = reinterpret_cast<const float4*>(p.s_init + state0 + (size_t)row * DK + half * C);
+    float S[2][C];
 #pragma unroll
-        for (int j = 0; j < C / 4; ++j) {
-            const float4 x = src[j];
-            S[4 * j] = x.x; S[4 * j + 1] = x.y; S[4 * j + 2] = x.z; S[4 * j + 3] = x.w;
+    for (int q = 0; q < 2; ++q) {
+        if (p.s_init) {
+            const float4* src = reinterpret_cast<const float4*>(p.s_init + state0 + (size_t)rows[q] * DK + cq * C);
+#pragma unroll
+            for (int j = 0; j < C / 4; ++j) {
+                const float4 x = src[j];
+                S[q][4 * j] = x.x; S[q][4 * j + 1] = x.y; S[q][4 * j + 2] = x.z; S[q][4 * j + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < C; ++j) S[q][j] = 0.f;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < C; ++j) S[j] = 0.f;
     }
 
     // this thread's pieces of a block: token tid / KP, 8 bf16 values at (tid % KP) * 8
@@ -97,53 +104,89 @@ __global__ __launch_bounds__(prefill_threads<DV>()) void prefill_kernel(const Pr
         const int buf = blk & 1;
         if (blk + 1 < nblk) load_block((blk + 1) * TB);   // in flight while this block is folded
         const int ntok = min(TB, L - blk * TB);
+        // Within a block the registers hold S / c, with c the product of the
+        // block's decays so far: the decay then costs one multiply per token
+        // instead of one per state element, and the update is a single
+        // multiply-add per element. c is folded back in at the end of every
+        // block (and early, should it leave [2^-60, 2^60]).
+        float c = 1.f;
         for (int tk = 0; tk < ntok; ++tk) {
             float kr[C];
-            const float4* kt = reinterpret_cast<const float4*>(&ks[buf][tk][half * C]);
+            const float4* kt = reinterpret_cast<const float4*>(&ks[buf][tk][cq * C]);
 #pragma unroll
             for (int j = 0; j < C / 4; ++j) {
                 const float4 x = kt[j];
                 kr[4 * j] = x.x; kr[4 * j + 1] = x.y; kr[4 * j + 2] = x.z; kr[4 * j + 3] = x.w;
             }
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float u[2];
 #pragma unroll
-            for (int j = 0; j < C; ++j) acc[j & 3] = fmaf(S[j], kr[j], acc[j & 3]);
-            float u = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            // the row's other half sits in the neighbouring lane (quad permutation 1,0,3,2)
-            u += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u), 0xB1, 0xF, 0xF, true));
+            for (int q = 0; q < 2; ++q) {
+                float acc[2] = {0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < C; ++j) acc[j & 1] = fmaf(S[q][j], kr[j], acc[j & 1]);
+                u[q] = acc[0] + acc[1];
+                // the row's other quarters sit in the lanes of the same quad
+                u[q] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u[q]), 0xB1, 0xF, 0xF, true));  // lane ^ 1
+                u[q] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u[q]), 0x4E, 0xF, 0xF, true));  // lane ^ 2
+            }
             const float a = as[buf][tk], bt = bs[buf][tk];
-            const float d = bt * (vsh[buf][tk][row] - a * u);
+            const float d0 = bt * (vsh[buf][tk][rows[0]] - a * (u[0] * c));   // u * c = S k
+            const float d1 = bt * (vsh[buf][tk][rows[1]] - a * (u[1] * c));
+            c *= a;                                              // S' = c (S/c_prev + (d / c) k^T)
+            if (!(c >= 0x1p-60f && c <= 0x1p60f)) {              // (uniform) fold the scale in early
 #pragma unroll
-            for (int j = 0; j < C; ++j) S[j] = fmaf(a, S[j], d * kr[j]);
+                for (int j = 0; j < C; ++j) {
+                    S[0][j] *= c;
+                    S[1][j] *= c;
+                }
+                c = 1.f;
+            }
+            const float rc = 1.f / c;
+            const float dc0 = d0 * rc, dc1 = d1 * rc;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                S[0][j] = fmaf(dc0, kr[j], S[0][j]);
+                S[1][j] = fmaf(dc1, kr[j], S[1][j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            S[0][j] *= c;
+            S[1][j] *= c;
         }
         if (blk + 1 < nblk) stage_block(buf ^ 1);   // the other buffer was last read before the previous barrier
         __syncthreads();
     }
 
-    if (!PLANES) {
-        float4* dst = reinterpret_cast<float4*>(p.s_out + state0 + (size_t)row * DK + half * C);
 #pragma unroll
-        for (int j = 0; j < C / 4; ++j) dst[j] = make_float4(S[4 * j], S[4 * j + 1], S[4 * j + 2], S[4 * j + 3]);
-    } else {
-        // fragment f = (w*KS + kk)*64 + lane holds S[16w + lane%16][32kk + 8(lane/16) + 0..7]
-        constexpr int KS = DK / 32;
-        uint16_t* pl = p.planes + ((size_t)p.slot[seq] * H + h) * 2 * DV * DK;
-        const int w = row / 16;
+    for (int q = 0; q < 2; ++q) {
+        const int row = rows[q];
+        if (!PLANES) {
+            float4* dst = reinterpret_cast<float4*>(p.s_out + state0 + (size_t)row * DK + cq * C);
 #pragma unroll
-        for (int g8 = 0; g8 < C / 8; ++g8) {
-            const int col = half * C + g8 * 8;
-            const int kk = col / 32, lane = (row % 16) + 16 * ((col % 32) / 8);
-            const size_t f = ((size_t)w * KS + kk) * 64 + lane;
-            uint32_t hi[8], lo[8];
+            for (int j = 0; j < C / 4; ++j)
+                dst[j] = make_float4(S[q][4 * j], S[q][4 * j + 1], S[q][4 * j + 2], S[q][4 * j + 3]);
+        } else {
+            // fragment f = (w*KS + kk)*64 + lane holds S[16w + lane%16][32kk + 8(lane/16) + 0..7]
+            constexpr int KS = DK / 32;
+            uint16_t* pl = p.planes + ((size_t)p.slot[seq] * H + h) * 2 * DV * DK;
+            const int w = row / 16;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                hi[e] = f32_to_bf16_rne(S[g8 * 8 + e]);
-                lo[e] = f32_to_bf16_rne(S[g8 * 8 + e] - __uint_as_float(hi[e] << 16));
+            for (int g8 = 0; g8 < C / 8; ++g8) {
+                const int col = cq * C + g8 * 8;
+                const int kk = col / 32, lane = (row % 16) + 16 * ((col % 32) / 8);
+                const size_t f = ((size_t)w * KS + kk) * 64 + lane;
+                uint32_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    hi[e] = f32_to_bf16_rne(S[q][g8 * 8 + e]);
+                    lo[e] = f32_to_bf16_rne(S[q][g8 * 8 + e] - __uint_as_float(hi[e] << 16));
+                }
+                *reinterpret_cast<uint4*>(pl + f * 8) = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                                                   hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+                *reinterpret_cast<uint4*>(pl + DV * DK + f * 8) = make_uint4(
+                    lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
             }
-            *reinterpret_cast<uint4*>(pl + f * 8) =
-                make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-            *reinterpret_cast<uint4*>(pl + DV * DK + f * 8) =
-                make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
         }
     }
 }
