@@ -190,6 +190,70 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     }
 
 
+def probe_leg(shape, q, k, S0):
+    """The box's practical peaks and the projection on its own.
+
+    copy: a 1 GiB device-to-device copy (2 GiB moved per launch); MFMA loop:
+    1024 workgroups x 8 waves x 2000 x 8 register-only 16x16x32 bf16 MFMAs;
+    projection: S0 [k q] of the step-1 vectors for all (request, head) pairs
+    with the step kernel's tiling (onela_probe_projection), repeated so that
+    its 96 MB of operands come from the 256 MB last-level cache, which is the
+    projection-only measurement the HBM-bound fused step cannot give.
+    """
+    import torch
+
+    from linear_attention_beam_gdn_amd import probes
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=q[0].device)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: probes.copy(src, dst), 10)
+    copy_gbs = 2 * n * 4 / t_copy / 1e9
+    del src, dst
+    n_wg, iters = 1024, 2000
+    buf = torch.empty(n_wg * 512, dtype=torch.float32, device=q[0].device)
+    t_mfma = timed(lambda: probes.mfma_loop(buf, n_wg, iters), 5)
+    loop_tflops = n_wg * 8 * iters * 8 * 16384 / t_mfma / 1e12
+    R, H, W, dk, dv = shape.R, shape.H, shape.W, shape.dk, shape.dv
+    colsum = torch.empty((R * H, dv), dtype=torch.float32, device=q[0].device)
+    t_proj = timed(lambda: probes.projection(S0, k[0], q[0], W, colsum), 20)
+    t_res = timed(lambda: probes.projection(S0, k[0], q[0], W, colsum, resident_pairs=8), 20)
+    flops = R * H * 2 * W * 2 * dv * dk
+    tflops = flops / t_proj / 1e12
+    res_tflops = flops / t_res / 1e12
+    operands = R * W * H * 2 * dk * 2 + R * H * dv * dk * 4          # k, q (bf16) and S0
+    p_bytes = R * 2 * W * H * dv * 4                                  # P itself, were it written in float32
+    cap = lambda nbytes: flops / (nbytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS
+    return ({"copy_gbs": copy_gbs, "copy_bytes_per_launch": 2 * n * 4, "mfma_loop_tflops": loop_tflops,
+             "mfma_loop_frac_of_peak": loop_tflops / BF16_PEAK_TFLOPS},
+            {"method": "projection-only probe (onela_probe_projection): the step kernel's 16x16x32 bf16 tiles and "
+                       "split-bf16 S0, k and q staged through LDS 64 beams at a time (next chunk in flight), per-row "
+                       "sums in place of the replay; all 512 (request, head) pairs, 2W = 512 vectors each. "
+                       "'achieved' reads the operands of 8 pairs only (workgroup p reads pair p mod 8), which stay "
+                       "in L2: the projection's matrix-core rate; 'full_footprint' streams all 96 MB of operands",
+             "us_per_launch": t_res * 1e6,
+             "algorithmic_gflop_per_launch": flops / 1e9,
+             "achieved_tflops": res_tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": res_tflops / BF16_PEAK_TFLOPS,
+             "issued_tflops": 2 * res_tflops, "issued_frac": 2 * res_tflops / BF16_PEAK_TFLOPS,
+             "issued_frac_of_measured_mfma_loop": 2 * res_tflops / loop_tflops,
+             "full_footprint": {"us_per_launch": t_proj * 1e6, "achieved_tflops": tflops,
+                                "frac": tflops / BF16_PEAK_TFLOPS, "issued_frac": 2 * tflops / BF16_PEAK_TFLOPS,
+                                "operand_gbs": operands / t_proj / 1e9},
+             "hbm_cap_frac": {"operands_from_hbm": cap(operands), "operands_and_fp32_P": cap(operands + p_bytes),
+                              "in_fused_step_S0_only": cap(R * H * dv * dk * 4)}})
+
+
 def fused_leg(shape, ep, q, k, v, al, be, par, S0, bytes_t, runs=20):
     """The same decode steps through onela_step_raw (input-side fusion: q, k
     normalised, alpha and beta formed from raw projections inside the launch,
@@ -425,6 +489,7 @@ def main():
                     help="S0 folded on the GPU from a synthetic prompt (default) or drawn N(0, 0.05^2)")
     ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
     ap.add_argument("--no-fused", action="store_true", help="skip the input-side fusion leg")
+    ap.add_argument("--no-probes", action="store_true", help="skip the copy / MFMA-loop / projection probes")
     ap.add_argument("--layers", type=int, default=4,
                     help="layers of the multi-layer decode-step leg (eager vs HIP graph); 0 skips it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -480,7 +545,7 @@ def main():
     prefill_out = None
     if args.s0 == "prompt":
         S0_dev, prefill_out = prompt_s0(lay, shape, args.prompt_len, reqs, dev, stream,
-                                        need_f32=not (args.no_fullstate and args.no_fused) or args.layers > 0)
+                                        need_f32=not (args.no_fullstate and args.no_fused and args.no_probes) or args.layers > 0)
         s0_label = (f"prompt-derived: the GDN recurrence over {args.prompt_len} synthetic tokens per request "
                     "and head, folded on the GPU (prefill_kernel)")
     else:
@@ -560,15 +625,13 @@ def main():
             "kernel": KERNEL_NAME,
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
-        "mfma_projection": {
-            "achieved_tflops": proj_tflops,
-            "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac": proj_tflops / BF16_PEAK_TFLOPS,
-            "note": "S0 projection flops of the fused launch over its whole duration (the launch is HBM-bound); "
-                    "issued MFMA work is 2x (split-bf16 S0)",
-        },
         "input_generation_s": round(t_gen, 1),
     }
+    if not args.no_probes:
+        out["probes"], out["mfma_projection"] = probe_leg(shape, q, k, S0_dev if S0_dev is not None else up(ep["S0"]))
+        out["mfma_projection"]["in_fused_step"] = {
+            "achieved_tflops": proj_tflops, "frac": proj_tflops / BF16_PEAK_TFLOPS,
+            "note": "the projection's flops over the whole fused launch, which HBM bounds"}
     if prefill_out is not None:
         out["prefill"] = prefill_out
     mem = lay.memory()

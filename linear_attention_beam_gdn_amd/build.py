@@ -1,4 +1,5 @@
-"""Build libonela.so (the C-ABI library of the OneLA GDN decode step) for gfx950.
+"""Build libonela.so (the C-ABI library of the OneLA GDN decode step) and
+libonela_probes.so (the measurement probes of bench.py) for gfx950.
 
 Run `python -m linear_attention_beam_gdn_amd.build`. It always recompiles and
 writes the library next to this file, so it travels with the source tree.
@@ -15,6 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libonela.so")
+PROBE_LIB = os.path.join(PKG, "libonela_probes.so")   # measurement probes of bench.py
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -30,6 +32,7 @@ HIPCC_FLAGS = [
 ]
 SOURCES = ["onela_kernels.hip", "onela_api.cpp", "fullstate_kernels.hip", "fullstate_api.cpp",
            "prefill_kernels.hip", "prefill_api.cpp"]
+PROBE_SOURCES = ["probes.hip"]
 
 
 def hipcc() -> str:
@@ -39,18 +42,23 @@ def hipcc() -> str:
     return path
 
 
+def _link(cc, sources, lib, verbose):
+    objs = []
+    for src in sources:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = lib + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False) -> str:
+    """Build libonela.so (the decode path) and libonela_probes.so (bench probes)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    _link(cc, SOURCES, LIB, verbose)
+    _link(cc, PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

@@ -30,3 +30,19 @@ def test_library_exports_every_declared_symbol():
     assert lib.onela_status_string(0) == b"ok"
     lib.onela_last_error.restype = ctypes.c_char_p
     assert lib.onela_last_error(None) == b""
+
+
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "onela_probes.h")
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from linear_attention_beam_gdn_amd import probes
+
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(onela_[a-z_]+)\s*\(", text)))
+    assert names == sorted(probes.EXPORTED)
+    if not os.path.exists(probes.PROBE_LIB_PATH):
+        pytest.skip("libonela_probes.so not built")
+    lib = ctypes.CDLL(probes.PROBE_LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
