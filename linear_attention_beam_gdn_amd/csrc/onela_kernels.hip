@@ -2,8 +2,10 @@
 //
 // One launch per decode step of one GDN layer (OneLA abstract: a fused GPU
 // kernel reuses the shared state across beams). A workgroup owns one
-// (request, head) pair and a range of beams, which it walks in chunks of
-// kChunk beams. For each chunk it
+// (request, head) pair and a range of beams. It first derives the request's
+// beam processing order for this step (beams grouped by ancestry, so that a
+// chunk gathers records other chunks mostly do not need), then walks its
+// range in that order in chunks of kChunk beams. For each chunk it
 //   A. stages k_t and q_t of the chunk's beams in LDS and builds each beam's
 //      ancestry row from its parent's row (record ids only; OneLA abstract:
 //      records are never moved or copied);
@@ -20,7 +22,14 @@
 // Wave w of the workgroup owns rows [16w, 16w+16) of d_v: its slice of S0
 // stays in registers as MFMA A-fragments for the whole beam loop, and every
 // step after the projection is row-separable, so no wave needs another
-// wave's rows.
+// wave's rows. After the beam loop the alpha records and (one head per
+// request, unless the index belongs to another layer's context) the next
+// step's ancestry rows are written in beam-index order.
+//
+// Variants: in graph mode each request's step index comes from device
+// memory and the last workgroup of the request advances it; the FUSED
+// instantiation takes raw projections (per-head L2 normalisation of q and k,
+// the decay and write-strength gates) and writes o as bf16.
 #include "onela_internal.h"
 
 namespace onela {
@@ -259,8 +268,9 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     // are near each other; a chunk then gathers mostly records that no other
     // chunk needs. The order only decides which beams share a chunk; each
     // beam's arithmetic is independent of it. Every workgroup of a request
-    // derives the same order (a deterministic rank), and one writes it for
-    // the next step. Wider beam sets than kOrderMax keep the natural order.
+    // derives the same order (a deterministic rank), and one workgroup of the
+    // index owner writes it for the next step. Wider beam sets than
+    // kOrderMax keep the natural order.
     if (ordered) {
         if (depth == 0) {
             for (int i = tid; i < W; i += NT) ord_s[i] = i;

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import gpu_harness as gh
     from linear_attention_beam_gdn_amd import Onela, OnelaError
-    from workload import shape_of
+    from workload import make_raw_episode, shape_of
 
 LAYERS = [(4, 128), (2, 64)]   # (heads, head dim); layer 0 owns the ancestry index
 KEYS = ("q", "k", "v", "alpha", "beta")
@@ -116,3 +116,51 @@ def test_graph_mode_switch_keeps_counters():
     assert e.value.status == -3
     lay.close()
     ref["layer"].close()
+
+
+def test_graph_replay_of_the_fused_step():
+    """onela_step_raw captured once in graph mode and replayed per step equals
+    the eager calls bit for bit."""
+    shape = shape_of(1, name="graph_fused", R=2, H=3, T=3)
+    ep = make_raw_episode(shape)
+    n, W, T = 2, shape.W, shape.T
+    keys = ("q_raw", "k_raw", "v", "a_raw", "b_raw")
+    A, D = gh.to_dev(ep["A_log"]), gh.to_dev(ep["dt_bias"])
+    src = {key: [gh.to_dev(ep[key][t]) for t in range(T)] for key in keys}
+    par_src = [gh.to_dev(np.maximum(ep["parents"][t], 0).astype(np.int32)) for t in range(T)]
+
+    eager = Onela(n, shape.H, 128, 128, W, T)
+    for i in range(n):
+        eager.init_request(i, gh.to_dev(ep["S0"][i]))
+    o16 = torch.empty((n * W, shape.H, 128), dtype=torch.int16, device=gh.dev())
+    want = []
+    for t in range(T):
+        eager.step_raw([0, 1], *[src[key][t] for key in keys], A, D, par_src[t], o16)
+        eager.sync()
+        want.append(o16.cpu().numpy().copy())
+    eager.close()
+
+    s = torch.cuda.Stream()
+    lay = Onela(n, shape.H, 128, 128, W, T, stream=s)
+    lay.set_graph_mode(True)
+    for i in range(n):
+        lay.init_request(i, gh.to_dev(ep["S0"][i]))
+    buf = {key: torch.empty_like(src[key][0]) for key in keys}
+    par = torch.empty_like(par_src[0])
+    out = torch.empty_like(o16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lay.step_raw([0, 1], *[buf[key] for key in keys], A, D, par, out)
+    for t in range(T):
+        with torch.cuda.stream(s):
+            for key in keys:
+                buf[key].copy_(src[key][t])
+            par.copy_(par_src[t])
+        g.replay()
+        s.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want[t]), t
+    lay.sync()
+    assert lay.get_step(1) == T
+    del g
+    lay.close()
