@@ -12,9 +12,12 @@ of the 5 steps are resident in HBM before timing starts.
 
 Prints one JSON line: beam-steps/s (value), microseconds per decode step, the
 per-depth breakdown, the HBM roofline fraction of the step kernel (algorithmic
-bytes per launch over its average duration from HIP events recorded around
-every launch in the timed region) and the float64 oracle timed on a bounded
-sample on the host cores.
+bytes per launch over its average duration: one pair of HIP events brackets
+the timed region's back-to-back launches on their stream) and the float64
+oracle timed on a bounded sample on the host cores. The per-depth breakdown
+comes from a separate pass with events around every launch: each event is a
+marker the GPU processes between two kernels, so that pass runs a few
+microseconds slower per launch and stays out of the timed region.
 """
 from __future__ import annotations
 
@@ -38,7 +41,155 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 KERNEL_NAME = "step_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_r32_h16_w256_t5_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "step_kernel_r32_h16_w256_t5_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_beam_gdn_amd", "csrc", "onela_kernels.hip")
+
+
+# --------------------------------------------------------------- counters
+# Kernels summarised from counter runs of this bench, by a fragment of their names.
+COUNTER_KERNELS = [
+    ("step_kernel<128, 128, false>", "::step_kernel<128, 128, false>"),
+    ("step_kernel<128, 128, true> (raw projections in)", "::step_kernel<128, 128, true>"),
+    ("prefill_kernel<128, 128, true> (5120-token prompts)", "::prefill_kernel<128, 128, true>"),
+    ("projection probe, operands streamed", "projection_kernel"),
+    ("projection probe, operands L2-resident", "projection_kernel"),
+    ("MFMA loop probe", "mfma_loop_kernel"),
+    ("copy probe", "::copy_kernel"),
+]
+
+
+def counters_from(dirs, command: str) -> str:
+    """Summarise rocprofv3 --pmc runs of this bench (one counter set per run,
+    each with GRBM_GUI_ACTIVE) into COUNTERS_FILE and return its text.
+
+    Per kernel, averaged over its dispatches: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES
+    over (GRBM_GUI_ACTIVE per XCD x SIMDs); LDS busy = SQ_LDS_IDX_ACTIVE over
+    (GRBM_GUI_ACTIVE per XCD x CUs); bank-conflict share = SQ_LDS_BANK_CONFLICT
+    over SQ_LDS_IDX_ACTIVE; wave time waiting / issuing = SQ_WAIT_ANY /
+    SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES; instructions per wave from SQ_INSTS_*
+    over SQ_WAVES. The projection probe's dispatches are split in launch order:
+    the bench runs the streamed form first, then the L2-resident one.
+    """
+    import csv
+    import glob
+
+    agent, per, n_disp = {}, {}, {}   # per[label][counter] -> list of per-dispatch values
+    for d in dirs:
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                rows.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Name", "").startswith("gfx"):
+                    agent = {k: int(r[k]) for k in ("Simd_Count", "Cu_Count", "Num_Xcc")}
+        for label, frag in COUNTER_KERNELS:
+            disp = [c for (i, n), c in sorted(rows.items()) if frag in n]
+            if frag == "projection_kernel":
+                half = len(disp) // 2
+                disp = disp[:half] if "streamed" in label else disp[half:]
+            n_disp[label] = max(n_disp.get(label, 0), len(disp))
+            for c in disp:
+                for name, v in c.items():
+                    per.setdefault(label, {}).setdefault(name, []).append(v)
+                if "GRBM_GUI_ACTIVE" in c and agent:
+                    g = c["GRBM_GUI_ACTIVE"] / agent["Num_Xcc"]
+                    derived = per.setdefault(label, {})
+                    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                        derived.setdefault("mfma_busy", []).append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * agent["Simd_Count"]))
+                    if "SQ_LDS_IDX_ACTIVE" in c:
+                        derived.setdefault("lds_busy", []).append(c["SQ_LDS_IDX_ACTIVE"] / (g * agent["Cu_Count"]))
+    if not agent:
+        raise SystemExit("no agent information under the counter directories")
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    head = ("| kernel | dispatches | MFMA busy | LDS busy | LDS bank-conflict share | wave time waiting | "
+            "wave time issuing | VALU / wave | MFMA / wave | LDS / wave | VMEM rd / wave | VMEM wr / wave | "
+            "bf16 MFMA GFLOP / dispatch |")
+    lines = [head, "|" + "---|" * (head.count("|") - 1)]
+    for label, _ in COUNTER_KERNELS:
+        c = {k: mean(v) for k, v in per.get(label, {}).items()}
+        if not c:
+            continue
+        waves = c.get("SQ_WAVES", float("nan"))
+        ratio = lambda a, b: c[a] / c[b] if c.get(a) is not None and c.get(b) else float("nan")
+        lines.append(
+            f"| {label} | {n_disp[label]} | {100 * c.get('mfma_busy', float('nan')):.1f}% | "
+            f"{100 * c.get('lds_busy', float('nan')):.1f}% | {100 * ratio('SQ_LDS_BANK_CONFLICT', 'SQ_LDS_IDX_ACTIVE'):.1f}% | "
+            f"{100 * ratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'):.0f}% | {100 * ratio('SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES'):.0f}% | "
+            f"{c.get('SQ_INSTS_VALU', float('nan')) / waves:.0f} | {c.get('SQ_INSTS_MFMA', float('nan')) / waves:.0f} | "
+            f"{c.get('SQ_INSTS_LDS', float('nan')) / waves:.0f} | {c.get('SQ_INSTS_VMEM_RD', float('nan')) / waves:.0f} | "
+            f"{c.get('SQ_INSTS_VMEM_WR', float('nan')) / waves:.0f} | "
+            f"{c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', float('nan')) * 512 / 1e9:.2f} |")
+    step = {k: mean(v) for k, v in per.get(COUNTER_KERNELS[0][0], {}).items()}
+    sratio = lambda a, b: step[a] / step[b] if step.get(a) is not None and step.get(b) else float("nan")
+    text = "\n".join([
+        "# Hardware counters of the decode-step kernels and the probes (rocprofv3 --pmc, one MI355X;",
+        "# r32_h16_d128_w256_t5 for the step kernels, all depths averaged)",
+        f"# commands (one counter set per run): {command}",
+        f"kernel_source_sha = {kernel_source_sha()}",
+        f"agent = {agent}",
+        f"step_kernel_mfma_busy = {step.get('mfma_busy', float('nan')):.4f}",
+        f"step_kernel_lds_bank_conflict_share = {sratio('SQ_LDS_BANK_CONFLICT', 'SQ_LDS_IDX_ACTIVE'):.4f}",
+        f"step_kernel_wave_time_waiting = {sratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'):.4f}",
+        "",
+        *lines,
+        "",
+    ])
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    open(COUNTERS_FILE, "w").write(text)
+    return text
+
+
+def read_counters():
+    """The step kernel's counter summary, if taken on this kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.lstrip().startswith(("#", "|")):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return {"mfma_busy": float(kv["step_kernel_mfma_busy"]),
+                "lds_bank_conflict_share": float(kv["step_kernel_lds_bank_conflict_share"]),
+                "wave_time_waiting": float(kv["step_kernel_wave_time_waiting"]),
+                "source": os.path.relpath(COUNTERS_FILE, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- timing
+def time_episodes(run, stream, episodes: int, T: int, instrumented: int = 10):
+    """run(events) enqueues one episode of T launches on `stream`; events is
+    None, or T (start, end) HIP event pairs to record around the launches.
+
+    Returns the mean launch duration in seconds over `episodes` back-to-back
+    episodes bracketed by one pair of HIP events (nothing else enqueued
+    between the launches), the wall time per episode in seconds, and the
+    median duration per depth in microseconds from a separate pass of
+    `instrumented` episodes with events around every launch."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(episodes):
+        run(None)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_launch_s = e0.elapsed_time(e1) * 1e-3 / (episodes * T)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+           for _ in range(instrumented)]
+    for i in range(instrumented):
+        run(evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[evs[i][t][0].elapsed_time(evs[i][t][1]) for t in range(T)] for i in range(instrumented)]) * 1e3
+    return mean_launch_s, wall / episodes, np.median(per, axis=0)
+
 
 
 # ------------------------------------------------------------- accounting
@@ -167,12 +318,14 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     toks = prompt_tokens_device(pshape, dev, reqs=reqs)
     args = (toks["k"], toks["v"], toks["alpha"], toks["beta"])
     lay.init_requests_from_prompts(reqs, *args)       # warm-up (and the state the bench decodes from)
+    reps = 5
     ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
     ev[0].record(stream)
-    lay.init_requests_from_prompts(reqs, *args)
+    for _ in range(reps):                             # each launch folds the same prompts again
+        lay.init_requests_from_prompts(reqs, *args)
     ev[1].record(stream)
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1])
+    ms = ev[0].elapsed_time(ev[1]) / reps
     S0 = prefill(*args, stream=stream) if need_f32 else None
     torch.cuda.synchronize()
     del toks, args
@@ -181,7 +334,8 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     return S0, {
         "kernel": "prefill_kernel",
         "what": f"S0 of {len(reqs)} requests x {shape.H} heads from {prompt_len}-token prompts, one launch "
-                "(onela_init_requests_from_prompts, written as the step kernel's bf16 planes)",
+                "(onela_init_requests_from_prompts, written as the step kernel's bf16 planes); mean of 5 "
+                "back-to-back launches",
         "ms": ms,
         "tokens_per_s": len(reqs) * prompt_len / (ms * 1e-3),
         "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -276,31 +430,30 @@ def fused_leg(shape, ep, q, k, v, al, be, par, S0, bytes_t, runs=20):
     D = torch.from_numpy(g["dt_bias"]).cuda()
     o16 = torch.empty((R * W, H, shape.dv), dtype=torch.int16, device=q[0].device)
     reqs = list(range(R))
-    # no synchronisation inside the timed loop: the queue stays ahead of the
-    # GPU, so the events bracket the launches and not the host's enqueueing
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
-          for _ in range(runs + 2)]
-    for it in range(runs + 2):
+
+    def episode(events):
         for r in reqs:
             lay.reset(r)
         for t in range(T):
-            ev[it][t][0].record(stream)
+            if events is not None:
+                events[t][0].record(stream)
             lay.step_raw(reqs, q[t], k[t], v[t], al[t], be[t], A, D, par[t], o16)
-            ev[it][t][1].record(stream)
-    torch.cuda.synchronize()
-    per = [[ev[it][t][0].elapsed_time(ev[it][t][1]) * 1e3 for t in range(T)] for it in range(2, runs + 2)]
+            if events is not None:
+                events[t][1].record(stream)
+
+    for _ in range(2):
+        episode(None)
+    mean_s, _, us = time_episodes(episode, stream, runs, T)
     lay.sync()
     lay.close()
-    us = np.median(np.array(per), axis=0)
     nbytes = [b["total"] - R * W * H * 2 * shape.dv for b in bytes_t]     # o at 2 B instead of 4
-    mean_s = float(np.mean(np.array(per))) * 1e-6
     gbs = float(np.mean(nbytes)) / mean_s / 1e9
     return {
         "what": "onela_step_raw: per-head q/k L2 normalisation, alpha = exp(-exp(A_log) softplus(a + dt_bias)), "
                 "beta = sigmoid(b) inside the launch, o as bf16",
         "kernel": "step_kernel<128, 128, true>",
         "kernel_us_mean": mean_s * 1e6,
-        "us_by_depth": [round(float(x), 2) for x in us],
+        "us_by_depth_instrumented": [round(float(x), 2) for x in us],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": float(np.mean(nbytes))},
     }
@@ -311,8 +464,8 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
     one HIP graph per decode step (graph mode: step counters on the device).
 
     Every layer gets the same inputs (the cost does not depend on their
-    values). Returns microseconds per decode step (all layers), medians over
-    the episodes, per depth and on average.
+    values). Returns microseconds per decode step (all layers), the median
+    over the episodes of each episode's time divided by its T steps.
     """
     import torch
 
@@ -333,22 +486,23 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
             lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t] if t else par[1], o)
 
     def run(replay):
-        # no synchronisation inside the timed loop (the queue stays ahead of the GPU)
-        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+        # one event pair per episode around its decode steps (the resets, which
+        # launch counter updates in graph mode, stay outside); no
+        # synchronisation inside the loop: the queue stays ahead of the GPU
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
               for _ in range(episodes + 2)]
         for it in range(episodes + 2):
             for lay in layers:
                 for r in reqs:
                     lay.reset(r)
+            ev[it][0].record(s)
             for t in range(T):
-                ev[it][t][0].record(s)
                 replay(t)
-                ev[it][t][1].record(s)
+            ev[it][1].record(s)
         s.synchronize()
-        per = [[ev[it][t][0].elapsed_time(ev[it][t][1]) * 1e3 for t in range(T)] for it in range(2, episodes + 2)]
         for lay in layers:
             lay.sync()
-        return np.median(np.array(per), axis=0)
+        return float(np.median([ev[it][0].elapsed_time(ev[it][1]) for it in range(2, episodes + 2)])) * 1e3 / T
 
     with torch.cuda.stream(s):
         eager = run(decode_step)
@@ -368,10 +522,8 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
         "what": f"one decode step of {n_layers} GDN layers sharing one ancestry index (all {R} requests), "
                 "eager onela_step calls vs one captured HIP graph per decode step",
         "layers": n_layers,
-        "eager_us_per_decode_step": float(eager.mean()),
-        "graph_us_per_decode_step": float(graph.mean()),
-        "eager_us_by_depth": [round(float(x), 1) for x in eager],
-        "graph_us_by_depth": [round(float(x), 1) for x in graph],
+        "eager_us_per_decode_step": eager,
+        "graph_us_per_decode_step": graph,
     }
 
 
@@ -497,7 +649,13 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic file and exit")
     ap.add_argument("--traffic-command", default="", help="command recorded in the traffic file")
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs of this bench into the counters file and exit")
+    ap.add_argument("--counters-command", default="", help="commands recorded in the counters file")
     args = ap.parse_args()
+    if args.counters_from:
+        print(counters_from(args.counters_from, args.counters_command))
+        return
     if args.traffic_from:
         print(traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.copy_probe or 256,
                                     args.traffic_command))
@@ -569,27 +727,19 @@ def main():
     lay.sync()
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        episode(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # Timed region: args.steps episodes back to back, bracketed by
+    # synchronisations and one pair of HIP events on the launch stream.
+    mean_launch_s, wall_per_episode, med_t_us = time_episodes(episode, stream, args.steps, T)
     lay.sync()
 
-    per_t_ms = np.array([[evs[i][t][0].elapsed_time(evs[i][t][1]) for t in range(T)] for i in range(args.steps)])
-    med_t_us = np.median(per_t_ms, axis=0) * 1e3
-    mean_launch_s = per_t_ms.mean() * 1e-3
     bytes_t = [step_bytes(shape, ep["parents"], t + 1) for t in range(T)]
     flops_t = [step_flops(shape, t + 1) for t in range(T)]
     bytes_per_launch = float(np.mean([b["total"] for b in bytes_t]))
     achieved_gbs = bytes_per_launch / mean_launch_s / 1e9
     proj_tflops = float(np.mean([f["projection"] for f in flops_t])) / mean_launch_s / 1e12
 
-    ms_per_step = wall / args.steps * 1e3
-    value = R * W * T / (wall / args.steps)
+    ms_per_step = wall_per_episode * 1e3
+    value = R * W * T / wall_per_episode
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -612,7 +762,7 @@ def main():
             "step": "one episode = host rewind + 5 decode steps of one GDN layer, one launch each",
         },
         "us_per_decode_step": ms_per_step * 1e3 / T,
-        "us_per_decode_step_by_depth": [round(float(x), 2) for x in med_t_us],
+        "us_by_depth_instrumented": [round(float(x), 2) for x in med_t_us],
         "kernel_us_mean": mean_launch_s * 1e6,
         "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
         "roofline": {
@@ -624,7 +774,9 @@ def main():
             "traffic": traffic,
             "kernel": KERNEL_NAME,
             "algorithmic_bytes_per_launch": bytes_per_launch,
+            "launch_duration": "HIP events around the timed region's back-to-back launches, divided by their number",
         },
+        "counters": read_counters(),
         "input_generation_s": round(t_gen, 1),
     }
     if not args.no_probes:

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     constexpr int NT = 64 * NW;
     constexpr int KS = DK / 32;        // MFMA k-steps
     constexpr int NG = CH / 32;        // 32-beam groups per chunk
-    constexpr int XS = DK + 8;         // padded LDS row (bf16 elements): breaks bank aliasing
+    constexpr int XS = DK + 16;        // padded LDS row (bf16 elements): B-fragment reads free of bank conflicts
     constexpr int MT = CH / 16;        // 16-beam tiles per chunk
     constexpr int TPQ = NT / CH;       // threads per beam for k_t . q_t
     constexpr int EQ = DK / TPQ;       // elements per thread there
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     static_assert((2 * CH * (DK / 8)) % NT == 0 && (CH * (DV / 8)) % NT == 0, "whole stream loads per thread");
     constexpr int DBD = 2;             // depths whose delta gathers are in flight together
     constexpr int UPP = 2;             // dot-product units per wave whose key gathers are in flight together
-    constexpr int VS = DV + 8;         // padded LDS row of v (bf16 elements)
+    constexpr int VS = DV + 16;        // padded LDS row of v (bf16 elements)
     static_assert(DV % kRowsPerWave == 0 && DK % 32 == 0, "tile shape");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -661,8 +661,8 @@ __global__ __launch_bounds__(64) void set_counters_kernel(int32_t* steps, int32_
 size_t step_lds_bytes(int dk, int dv, int T_max, int W) {
     const size_t ms = T_max > 1 ? (size_t)T_max - 1 : 1;
     return kChunk * ms * 16                       // coef_s
-           + 2 * kChunk * (size_t)(dk + 8) * 2    // xs
-           + kChunk * (size_t)(dv + 8) * 2        // vs
+           + 2 * kChunk * (size_t)(dk + 16) * 2   // xs
+           + kChunk * (size_t)(dv + 16) * 2       // vs
            + kChunk * ms * 4                      // anc_s
            + 3 * kChunk * 4                       // kq_s, at_s, bt_s
            + (W <= kOrderMax ? (size_t)((W + 3) & ~3) * 4 : 0);   // ord_s

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(float* out, int iters) {
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void projection_kernel(
     const float* __restrict__ S0, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q, int H, int W,
     int resident, float* __restrict__ colsum) {
-    constexpr int DK = 128, DV = 128, KS = DK / 32, CH = 64, XS = DK + 8, SEG = DK / 8;
+    constexpr int DK = 128, DV = 128, KS = DK / 32, CH = 64, XS = DK + 16, SEG = DK / 8;
     constexpr int PIECES = (2 * CH * SEG) / 512;     // 16-byte pieces of a chunk per thread
     __shared__ __align__(16) uint16_t xs[2][2 * CH * XS];   // two chunk buffers
     const int src = resident ? (int)(blockIdx.x % resident) : (int)blockIdx.x;   // pair whose operands are read

@@ -61,6 +61,7 @@ def run_episode(shape, ep, S0, beams_per_block=0, keep_delta=True, reqs=None):
             outs["delta"].append(d.cpu().numpy().copy())
         outs["anc"].append(np.stack([lay.get_ancestry(r) for r in reqs]))
     outs["layer"] = lay
+    outs["reqs"] = reqs
     return outs
 
 

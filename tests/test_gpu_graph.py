@@ -60,10 +60,14 @@ def test_graph_replay_of_a_two_layer_decode_step():
         for li, lay in enumerate(layers):
             lay.step(list(range(n)), *[buf[li][key] for key in KEYS], par, outs[li])
 
+    def replay():
+        with torch.cuda.stream(s):                # after the fills and resets on s
+            g.replay()
+        s.synchronize()
+
     for t in range(T):
         fill(t)
-        g.replay()
-        s.synchronize()
+        replay()
         for li in range(len(layers)):
             assert np.array_equal(outs[li].cpu().numpy(), refs[li]["o"][t]), (li, t)
         torch.cuda.synchronize()
@@ -73,8 +77,7 @@ def test_graph_replay_of_a_two_layer_decode_step():
         assert lay.get_step(0) == T
     assert np.array_equal(owner.get_ancestry(1), refs[0]["anc"][-1][1])
 
-    g.replay()                                   # a fifth step: no record slot left
-    s.synchronize()
+    replay()                                     # a fifth step: no record slot left
     with pytest.raises(OnelaError) as e:
         owner.sync()
     assert e.value.status == -3
@@ -82,8 +85,7 @@ def test_graph_replay_of_a_two_layer_decode_step():
         for i in range(n):
             lay.reset(i)
     fill(0)
-    g.replay()
-    s.synchronize()
+    replay()
     for li, lay in enumerate(layers):
         lay.sync()
         assert lay.get_step(1) == 1
@@ -157,7 +159,7 @@ def test_graph_replay_of_the_fused_step():
             for key in keys:
                 buf[key].copy_(src[key][t])
             par.copy_(par_src[t])
-        g.replay()
+            g.replay()                            # on s, after the copies
         s.synchronize()
         assert np.array_equal(out.cpu().numpy(), want[t]), t
     lay.sync()

@@ -28,7 +28,7 @@ def _check_pairs(shape, ep, S0, outs, pairs, tol=None):
             anc = outs["anc"][t][i]
             np.testing.assert_array_equal(anc[:, :t], ref["anc"][t])
             assert np.all(anc[:, t:] == -1)
-        a, d, kbits = outs["layer"].get_records(i, h, T * W)
+        a, d, kbits = outs["layer"].get_records(outs["reqs"][i], h, T * W)
         sl = slice(i * W, (i + 1) * W)
         np.testing.assert_array_equal(a.reshape(T, W), ep["alpha"][:, sl, h])
         np.testing.assert_array_equal(kbits.reshape(T, W, -1), ep["k"][:, sl, h, :])
@@ -145,3 +145,15 @@ def test_requests_at_different_depths():
             for t in range(shape.T):
                 assert np.abs(o_hist[i][t][:, h] - ref["o"][t]).max() <= gh.TOL
     lay.close()
+
+
+def test_more_requests_than_one_launch():
+    """70 requests in one call (two launches per step, 64 + 6) under library
+    ids in reverse order; every (request, head) pair against the oracle."""
+    shape = shape_of(0, name="many_requests", R=70, H=2, dk=32, dv=32, W=8, T=3)
+    ep, S0 = gh.episode(shape)
+    reqs = [74 - i for i in range(70)]
+    print(f"[parity] {shape.name}: 70 requests, library ids 74..5", flush=True)
+    outs = gh.run_episode(shape, ep, S0, reqs=reqs)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(70) for h in range(2)])
+    outs["layer"].close()
