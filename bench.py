@@ -527,6 +527,67 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
     }
 
 
+def stress_leg(episodes=3):
+    """The stress workload: 64 requests x 32 heads, d = 128, W = 1024, T = 7,
+    Zipf(1.2) parents (deep shared ancestry), inputs drawn on the GPU for all
+    7 steps before timing (about 11 GB). Same timing method as the main leg:
+    one event pair around back-to-back episodes, per-depth durations from a
+    separate pass with events around every launch."""
+    import torch
+
+    from linear_attention_beam_gdn_amd import Onela
+    from workload.gen_device import all_parents, s0_device, step_inputs
+
+    shape = shape_of(4)
+    R, H, W, T, d = shape.R, shape.H, shape.W, shape.T, shape.dk
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    parents = all_parents(shape)
+    S0 = s0_device(shape, dev)
+    ins = [step_inputs(shape, t, dev) for t in range(T)]
+    par = [None] + [torch.from_numpy(parents[t].astype(np.int32)).to(dev) for t in range(1, T)]
+    lay = Onela(R, H, d, d, W, T, stream=stream)
+    for r in range(R):
+        lay.init_request(r, S0[r].contiguous())
+    del S0
+    o = torch.empty((R * W, H, d), dtype=torch.float32, device=dev)
+    reqs = list(range(R))
+
+    def episode(events):
+        for r in reqs:
+            lay.reset(r)
+        for t in range(T):
+            x = ins[t]
+            if events is not None:
+                events[t][0].record(stream)
+            lay.step(reqs, x["q"], x["k"], x["v"], x["alpha"], x["beta"], par[t], o)
+            if events is not None:
+                events[t][1].record(stream)
+
+    episode(None)
+    mean_s, wall, by_depth = time_episodes(episode, stream, episodes, T, instrumented=2)
+    lay.sync()
+    mem = lay.memory()
+    lay.close()
+    del ins, par, o
+    torch.cuda.empty_cache()
+    bytes_t = [step_bytes(shape, parents, t + 1) for t in range(T)]
+    nbytes = float(np.mean([b["total"] for b in bytes_t]))
+    gbs = nbytes / mean_s / 1e9
+    return {
+        "workload": shape.name,
+        "what": "64 requests x 32 heads, d = 128, W = 1024, T = 7, parents Zipf(1.2) over the previous beams",
+        "us_per_decode_step": wall / T * 1e6,
+        "beam_steps_per_s": R * W * T / wall,
+        "kernel_us_mean": mean_s * 1e6,
+        "us_by_depth_instrumented": [round(float(x), 1) for x in by_depth],
+        "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
+        "persistent_state_bytes": mem["s0_bytes"] + mem["record_bytes"] + mem["index_bytes"],
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes},
+    }
+
+
 def fullstate_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela_ms_per_step, onela_mem):
     """Same workload through the full-state comparator (a full state per beam)."""
     import torch
@@ -642,6 +703,8 @@ def main():
     ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
     ap.add_argument("--no-fused", action="store_true", help="skip the input-side fusion leg")
     ap.add_argument("--no-probes", action="store_true", help="skip the copy / MFMA-loop / projection probes")
+    ap.add_argument("--no-stress", action="store_true",
+                    help="skip the stress-workload leg (64 requests x 32 heads, W = 1024, T = 7)")
     ap.add_argument("--layers", type=int, default=4,
                     help="layers of the multi-layer decode-step leg (eager vs HIP graph); 0 skips it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -798,6 +861,8 @@ def main():
         out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o,
                                                     up(ep["S0"]) if S0_dev is None else S0_dev, stream,
                                                     mean_launch_s, ms_per_step, mem)
+    if not args.no_stress:
+        out["stress_workload"] = stress_leg()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)
     print(json.dumps(out), flush=True)
