@@ -527,6 +527,139 @@ def multi_layer_leg(shape, n_layers, q, k, v, al, be, par, S0, episodes=10):
     }
 
 
+def replay_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela_ms_per_step, onela_mem):
+    """Same workload through the replay comparator (every beam rebuilds its
+    state from S0 and its own ancestral records at every step)."""
+    import torch
+
+    from linear_attention_beam_gdn_amd import ReplayState
+
+    R, H, W, T = shape.R, shape.H, shape.W, shape.T
+    rs = ReplayState(R, H, shape.dk, shape.dv, W, T, stream=stream)
+    for r in range(R):
+        rs.init_request(r, S0[r].contiguous())
+    reqs = list(range(R))
+
+    def episode(events):
+        for r in reqs:
+            rs.reset(r)
+        for t in range(T):
+            if events is not None:
+                events[t][0].record(stream)
+            rs.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t], o)
+            if events is not None:
+                events[t][1].record(stream)
+
+    episode(None)
+    mean_s, wall, by_depth = time_episodes(episode, stream, 5, T, instrumented=2)
+    rs.sync()
+    rs_mem = rs.memory()
+    rs.close()
+    return {
+        "what": "the same decode steps with every beam rebuilding its d_v x d_k state from S0 and its own "
+                "ancestral records (full rank-one updates) at every step; nothing shared between beams",
+        "kernel_us_mean": mean_s * 1e6,
+        "us_per_decode_step": wall / T * 1e6,
+        "us_by_depth_instrumented": [round(float(x), 1) for x in by_depth],
+        "speedup_kernel": mean_s / onela_launch_s,
+        "speedup_step": wall / T * 1e3 / (onela_ms_per_step / T),
+        "persistent_state_bytes": {"replay": rs_mem,
+                                   "onela": onela_mem["s0_bytes"] + onela_mem["record_bytes"] + onela_mem["index_bytes"]},
+    }
+
+
+# Shapes of the operator sweep: beam width, head dimension, decode steps and
+# (requests, heads); parents chosen as the top W of 4W random scores.
+SWEEP_W = (64, 256, 1024)
+SWEEP_D = (64, 128)
+SWEEP_T = (3, 7)
+SWEEP_RH = ((4, 16), (32, 16))
+SWEEP_FS_MAX_BYTES = 40 << 30       # full-state stores above this are skipped
+
+
+def sweep_leg(episodes=2):
+    """OneLA against the full-state and replay comparators over a grid of
+    operator shapes (W x d x T x (requests, heads)), on seeded inputs drawn on
+    the GPU. Per shape: mean launch time of each path over `episodes`
+    episodes (one event pair), speedups, and the persistent-state reduction
+    against W full states per request and head. Returns the per-shape rows
+    and the medians over the shapes."""
+    import torch
+
+    from linear_attention_beam_gdn_amd import FullState, Onela, ReplayState
+    from workload.gen_device import all_parents, s0_device, step_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for (R, H) in SWEEP_RH:
+        for W in SWEEP_W:
+            for d in SWEEP_D:
+                for T in SWEEP_T:
+                    shape = shape_of(1, name=f"sweep_r{R}_h{H}_d{d}_w{W}_t{T}", R=R, H=H, dk=d, dv=d, W=W, T=T)
+                    parents = all_parents(shape)
+                    S0 = s0_device(shape, dev)
+                    ins = [step_inputs(shape, t, dev) for t in range(T)]
+                    par = [None] + [torch.from_numpy(parents[t].astype(np.int32)).to(dev) for t in range(1, T)]
+                    o = torch.empty((R * W, H, d), dtype=torch.float32, device=dev)
+                    reqs = list(range(R))
+
+                    def run(ctx):
+                        for r in reqs:
+                            ctx.init_request(r, S0[r].contiguous())
+
+                        def episode():
+                            for r in reqs:
+                                ctx.reset(r)
+                            for t in range(T):
+                                x = ins[t]
+                                ctx.step(reqs, x["q"], x["k"], x["v"], x["alpha"], x["beta"], par[t], o)
+
+                        episode()
+                        torch.cuda.synchronize()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(episodes):
+                            episode()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        ctx.sync()
+                        return e0.elapsed_time(e1) * 1e-3 / (episodes * T)
+
+                    ol = Onela(R, H, d, d, W, T, stream=stream)
+                    t_ol = run(ol)
+                    mem = ol.memory()
+                    ol.close()
+                    rs = ReplayState(R, H, d, d, W, T, stream=stream)
+                    t_rs = run(rs)
+                    rs.close()
+                    per_beam = R * H * W * d * d * 4
+                    t_fs = None
+                    if 2 * per_beam <= SWEEP_FS_MAX_BYTES:
+                        fs = FullState(R, H, d, d, W, T, stream=stream)
+                        t_fs = run(fs)
+                        fs.close()
+                    onela_bytes = mem["s0_bytes"] + mem["record_bytes"] + mem["index_bytes"]
+                    rows.append({"R": R, "H": H, "d": d, "W": W, "T": T, "onela_us": t_ol * 1e6,
+                                 "replay_us": t_rs * 1e6, "fullstate_us": None if t_fs is None else t_fs * 1e6,
+                                 "speedup_vs_replay": t_rs / t_ol,
+                                 "speedup_vs_fullstate": None if t_fs is None else t_fs / t_ol,
+                                 "state_reduction": per_beam / onela_bytes})
+                    del ins, par, o, S0
+                    torch.cuda.empty_cache()
+    med = lambda key: float(np.median([r[key] for r in rows if r[key] is not None]))
+    return {
+        "what": "mean launch time per decode step of OneLA, the replay comparator and the full-state comparator "
+                f"over {len(rows)} shapes (W in {SWEEP_W}, d in {SWEEP_D}, T in {SWEEP_T}, (requests, heads) in "
+                f"{SWEEP_RH}; top-W-of-4W parents); state reduction = W full float32 states per request and head "
+                "over OneLA's S0 planes + records + index",
+        "median_speedup_vs_replay": med("speedup_vs_replay"),
+        "median_speedup_vs_fullstate": med("speedup_vs_fullstate"),
+        "median_state_reduction": med("state_reduction"),
+        "shapes": rows,
+    }
+
+
 def stress_leg(episodes=3):
     """The stress workload: 64 requests x 32 heads, d = 128, W = 1024, T = 7,
     Zipf(1.2) parents (deep shared ancestry), inputs drawn on the GPU for all
@@ -703,6 +836,9 @@ def main():
     ap.add_argument("--prompt-len", type=int, default=5120, help="prompt tokens per request for --s0 prompt")
     ap.add_argument("--no-fused", action="store_true", help="skip the input-side fusion leg")
     ap.add_argument("--no-probes", action="store_true", help="skip the copy / MFMA-loop / projection probes")
+    ap.add_argument("--no-replay", action="store_true", help="skip the replay-comparator leg")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the operator sweep (OneLA vs both comparators over 24 shapes)")
     ap.add_argument("--no-stress", action="store_true",
                     help="skip the stress-workload leg (64 requests x 32 heads, W = 1024, T = 7)")
     ap.add_argument("--layers", type=int, default=4,
@@ -861,8 +997,14 @@ def main():
         out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o,
                                                     up(ep["S0"]) if S0_dev is None else S0_dev, stream,
                                                     mean_launch_s, ms_per_step, mem)
+    if not args.no_replay:
+        out["replay_comparator"] = replay_leg(shape, q, k, v, al, be, par, o,
+                                              up(ep["S0"]) if S0_dev is None else S0_dev, stream,
+                                              mean_launch_s, ms_per_step, mem)
     if not args.no_stress:
         out["stress_workload"] = stress_leg()
+    if not args.no_sweep:
+        out["operator_sweep"] = sweep_leg()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)
     print(json.dumps(out), flush=True)

@@ -290,6 +290,41 @@ onela_status onela_fs_sync(onela_fs_ctx* ctx);
 /* Device bytes of persistent state the comparator owns. */
 onela_status onela_fs_get_memory(const onela_fs_ctx* ctx, uint64_t* state_bytes);
 
+/* ---- comparator: every beam replays its own history ---------------------
+ * The replay-based serving path (OneLA review, evolve.pub, "Summary" and
+ * "Scope & Claims": the ReplaySSM baseline checkpoints the state only at the
+ * prompt boundary and treats every beam as an independent request that
+ * replays its shared history). At every step each beam starts from S0,
+ * applies its ancestral records (alpha_j, delta_j, k_j) oldest first as full
+ * rank-one updates S <- alpha_j S + delta_j k_j^T, takes the GDN step on the
+ * rebuilt d_v x d_k state and appends its record; nothing is shared between
+ * beams (not even S0 k) and no per-beam state persists: Theta(W t d_v d_k)
+ * work per step at depth t. Same recurrence, conventions, argument layouts
+ * and error behaviour as the onela_* calls above; the library owns S0 copies
+ * (float32), the record store (the same records onela_step appends) and the
+ * parents given at every step, allocated in onela_rs_create. Used to measure
+ * what sharing the projection saves.
+ */
+typedef struct onela_rs_ctx onela_rs_ctx;
+
+/* Allocates max_requests * (num_heads * (4 d_v d_k + max_steps * beam_width *
+ * (4 + 4 d_v + 2 d_k)) + 4 max_steps * beam_width) + 4 max_requests bytes. */
+onela_status onela_rs_create(const onela_config* cfg, void* hip_stream, onela_rs_ctx** out);
+onela_status onela_rs_destroy(onela_rs_ctx* ctx);
+/* Copies S0 (device float32 [H][d_v][d_k]) and rewinds the request to step 0. */
+onela_status onela_rs_init_request(onela_rs_ctx* ctx, int32_t req, const float* S0);
+/* One decode step; arguments as for onela_step. A parent index outside
+ * [0, W) poisons the request (reported by onela_rs_sync as
+ * ONELA_E_PARENT_RANGE), as in onela_step. */
+onela_status onela_rs_step(onela_rs_ctx* ctx, int32_t n_req, const int32_t* reqs,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* alpha, const float* beta,
+                           const int32_t* parent_idx, float* o, float* delta_out);
+onela_status onela_rs_reset(onela_rs_ctx* ctx, int32_t req);
+onela_status onela_rs_sync(onela_rs_ctx* ctx);
+/* Device bytes of persistent state the comparator owns (S0, records, parents). */
+onela_status onela_rs_get_memory(const onela_rs_ctx* ctx, uint64_t* state_bytes);
+
 /* Static text for a status code. */
 const char* onela_status_string(onela_status s);
 

@@ -31,7 +31,7 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["onela_kernels.hip", "onela_api.cpp", "fullstate_kernels.hip", "fullstate_api.cpp",
-           "prefill_kernels.hip", "prefill_api.cpp"]
+           "replay_kernels.hip", "replay_api.cpp", "prefill_kernels.hip", "prefill_api.cpp"]
 PROBE_SOURCES = ["probes.hip"]
 
 

@@ -74,6 +74,30 @@ struct FullStateParams {
     int32_t epoch[kMaxReqPerLaunch];
 };
 
+// Replay comparator: every beam rebuilds its state from S0 and its own
+// ancestral records at every step (no per-beam state is kept, nothing shared).
+struct ReplayParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* alpha;
+    const float* beta;
+    const int32_t* parent;      // this step's parents [n_req][W] (null at t = 1)
+    float* o;
+    float* delta_out;
+    const float* s0;            // [max_requests][H][DV*DK] float32
+    float* rec_alpha;           // [max_requests][H][T_max*W]
+    float* rec_delta;           // [max_requests][H][T_max*W][DV]
+    uint16_t* rec_k;            // [max_requests][H][T_max*W][DK] bf16
+    int32_t* par_hist;          // [max_requests][T_max][W]: row s = parents given at step s+1 (s >= 1)
+    int32_t* err;               // [max_requests]
+    int32_t H, W, T_max, max_requests;
+    int32_t n_req;
+    int32_t slot[kMaxReqPerLaunch];
+    int32_t t[kMaxReqPerLaunch];
+    int32_t epoch[kMaxReqPerLaunch];
+};
+
 // The prefill: one workgroup per (sequence, head) folds a prompt into a state.
 struct PrefillParams {
     const uint16_t* k;       // bf16 [n_seq][L][H][DK]
@@ -97,6 +121,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 // Returns hipErrorInvalidValue for unsupported (DK, DV).
 hipError_t launch_prefill(int dk, int dv, bool planes, const PrefillParams& p, hipStream_t s);
 hipError_t launch_fullstate_step(int dk, int dv, const FullStateParams& p, hipStream_t s);
+hipError_t launch_replay_step(int dk, int dv, const ReplayParams& p, hipStream_t s);
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
 hipError_t launch_step(int dk, int dv, bool fused, const StepParams& p, hipStream_t s);
 // Set the launch attributes the step kernel needs for this shape (once, before any launch).

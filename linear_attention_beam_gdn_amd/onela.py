@@ -30,7 +30,11 @@ EXPORTED = (
     "onela_sync", "onela_set_beams_per_block", "onela_get_step", "onela_get_ancestry",
     "onela_get_records", "onela_get_memory", "onela_status_string", "onela_last_error",
     "onela_fs_create", "onela_fs_destroy", "onela_fs_init_request", "onela_fs_step", "onela_fs_reset",
-    "onela_fs_sync", "onela_fs_get_memory", "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode", "onela_step_raw",
+    "onela_fs_sync", "onela_fs_get_memory",
+    "onela_rs_create", "onela_rs_destroy", "onela_rs_init_request", "onela_rs_step", "onela_rs_reset",
+    "onela_rs_sync", "onela_rs_get_memory",
+    "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode",
+    "onela_step_raw",
 )
 
 
@@ -82,6 +86,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_fs_reset": (i32, [vp, i32]),
         "onela_fs_sync": (i32, [vp]),
         "onela_fs_get_memory": (i32, [vp, vp]),
+        "onela_rs_create": (i32, [ctypes.POINTER(_Config), vp, ctypes.POINTER(vp)]),
+        "onela_rs_destroy": (i32, [vp]),
+        "onela_rs_init_request": (i32, [vp, i32, vp]),
+        "onela_rs_step": (i32, [vp, i32, p_i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "onela_rs_reset": (i32, [vp, i32]),
+        "onela_rs_sync": (i32, [vp]),
+        "onela_rs_get_memory": (i32, [vp, vp]),
         "onela_last_error": (ctypes.c_char_p, [vp]),
         "onela_init_requests_from_prompts": (i32, [vp, i32, p_i32, i32, vp, vp, vp, vp]),
         "onela_prefill": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
@@ -272,8 +283,10 @@ class Onela:
         return {"s0_bytes": s0.value, "record_bytes": rec.value, "index_bytes": idx.value}
 
 
-class FullState:
-    """The comparator that keeps a full d_v x d_k state per beam (same calls as Onela)."""
+class _Comparator:
+    """A comparator context: same calls as Onela, C functions named by PREFIX."""
+
+    PREFIX = ""
 
     def __init__(self, max_requests, num_heads, d_k, d_v, beam_width, max_steps, stream=None):
         import torch
@@ -283,18 +296,21 @@ class FullState:
         self.cfg = _Config(max_requests, num_heads, d_k, d_v, beam_width, max_steps)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self._ctx = ctypes.c_void_p()
-        st = self.lib.onela_fs_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.stream.cuda_stream),
-                                      ctypes.byref(self._ctx))
+        st = self._fn("create")(ctypes.byref(self.cfg), ctypes.c_void_p(self.stream.cuda_stream),
+                                ctypes.byref(self._ctx))
         if st != ONELA_OK:
-            raise OnelaError(st, "onela_fs_create")
+            raise OnelaError(st, f"{self.PREFIX}_create")
+
+    def _fn(self, name):
+        return getattr(self.lib, f"{self.PREFIX}_{name}")
 
     def _check(self, status, where):
         if status != ONELA_OK:
-            raise OnelaError(status, where)
+            raise OnelaError(status, f"{self.PREFIX}_{where}")
 
     def close(self):
         if self._ctx:
-            self.lib.onela_fs_destroy(self._ctx)
+            self._fn("destroy")(self._ctx)
             self._ctx = ctypes.c_void_p()
 
     def __del__(self):
@@ -306,7 +322,7 @@ class FullState:
     def init_request(self, req: int, S0):
         c = self.cfg
         p = _ptr(S0, "S0", (self._torch.float32,), (c.num_heads, c.d_v, c.d_k))
-        self._check(self.lib.onela_fs_init_request(self._ctx, req, p), "onela_fs_init_request")
+        self._check(self._fn("init_request")(self._ctx, req, p), "init_request")
 
     def step(self, reqs, q, k, v, alpha, beta, parent_idx, o, delta_out=None):
         torch = self._torch
@@ -316,7 +332,7 @@ class FullState:
         bf = (torch.bfloat16, torch.int16, torch.uint16)
         f32 = (torch.float32,)
         arr = (ctypes.c_int32 * n)(*[int(r) for r in reqs])
-        st = self.lib.onela_fs_step(
+        st = self._fn("step")(
             self._ctx, n, arr,
             _ptr(q, "q", bf, (rows, c.num_heads, c.d_k)),
             _ptr(k, "k", bf, (rows, c.num_heads, c.d_k)),
@@ -327,18 +343,31 @@ class FullState:
             _ptr(o, "o", f32, (rows, c.num_heads, c.d_v)),
             _ptr(delta_out, "delta_out", f32, (rows, c.num_heads, c.d_v), optional=True),
         )
-        self._check(st, "onela_fs_step")
+        self._check(st, "step")
 
     def reset(self, req: int):
-        self._check(self.lib.onela_fs_reset(self._ctx, req), "onela_fs_reset")
+        self._check(self._fn("reset")(self._ctx, req), "reset")
 
     def sync(self):
-        self._check(self.lib.onela_fs_sync(self._ctx), "onela_fs_sync")
+        self._check(self._fn("sync")(self._ctx), "sync")
 
     def memory(self) -> int:
         b = ctypes.c_uint64()
-        self._check(self.lib.onela_fs_get_memory(self._ctx, ctypes.byref(b)), "onela_fs_get_memory")
+        self._check(self._fn("get_memory")(self._ctx, ctypes.byref(b)), "get_memory")
         return b.value
+
+
+class FullState(_Comparator):
+    """The comparator that keeps a full d_v x d_k state per beam (onela_fs_*)."""
+
+    PREFIX = "onela_fs"
+
+
+class ReplayState(_Comparator):
+    """The comparator in which every beam rebuilds its state from S0 and its own
+    ancestral records at every step (onela_rs_*)."""
+
+    PREFIX = "onela_rs"
 
 
 def prefill(k, v, alpha, beta, S_init=None, out=None, stream=None):
