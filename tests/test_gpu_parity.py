@@ -99,6 +99,24 @@ def test_parity_wide_beam_sets(W, bpb):
     outs["layer"].close()
 
 
+def test_parity_extreme_gates():
+    """Gates at their ends mixed with ordinary draws: alpha = 0 forgets the
+    whole history, S0 included; alpha = 1 keeps it undecayed; beta = 0 writes
+    nothing, so delta is exactly zero; beta = 1 writes v back at the key."""
+    shape = shape_of(0, name="extreme_gates", R=2, H=3, dk=64, dv=64, W=40, T=6)
+    ep, S0 = gh.episode(shape)
+    rng = np.random.default_rng(11)
+    for key in ("alpha", "beta"):
+        pick = rng.integers(0, 3, size=ep[key].shape)
+        ep[key] = np.where(pick == 0, 0.0, np.where(pick == 1, 1.0, ep[key])).astype(np.float32)
+    print(f"[parity] {shape.name}", flush=True)
+    outs = gh.run_episode(shape, ep, S0)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(2) for h in range(3)])
+    for t in range(shape.T):
+        assert np.all(outs["delta"][t][ep["beta"][t] == 0] == 0)
+    outs["layer"].close()
+
+
 def test_tile_size_invariance_and_determinism():
     """Outputs are bit-identical across launch shapes and across runs."""
     shape = shape_of(1, R=2, T=4)

@@ -16,7 +16,7 @@ if torch.cuda.is_available():
     import gpu_harness as gh
     from linear_attention_beam_gdn_amd import Onela, OnelaError, load_library, prefill
     from oracle import prompt_state
-    from workload import bf16_bits_to_f32, prompt_tokens, shape_of
+    from workload import bf16_bits_to_f32, f32_to_bf16_bits, prompt_tokens, shape_of
     from workload.gen_device import prompt_tokens_device
 
 
@@ -78,6 +78,66 @@ def test_prefill_zero_length_and_split_prompts():
 
     assert torch.equal(whole, two_calls(32))
     assert (whole - two_calls(29)).abs().max().item() <= 1e-5
+
+
+def test_prefill_extreme_gates_and_repeated_keys():
+    """Gates at their ends and keys that repeat, where the chunk's triangular
+    system is least benign (unit entries below the diagonal)."""
+    shape = shape_of(0, name="prefill_gates", H=2, dk=64, dv=64)
+    L = 45
+    tok = _host_tokens(shape, 1, L)
+    gen = torch.Generator().manual_seed(5)
+    init = (0.05 * torch.randn((1, 2, 64, 64), generator=gen)).to(gh.dev())
+
+    # alpha = 1, beta = 0 on every token: nothing is written and the initial
+    # state comes back bit for bit
+    t1 = dict(tok, alpha=np.ones_like(tok["alpha"]), beta=np.zeros_like(tok["beta"]))
+    assert torch.equal(prefill(*_dev(t1), S_init=init), init)
+
+    # one unit key (four entries of 1/2, exact in bf16) on every token with
+    # alpha = beta = 1: each token overwrites the value stored at k, so the fold
+    # is S_init (I - k k^T) + v_L k^T
+    kvec = np.zeros((2, 64))
+    kvec[0, [3, 17, 40, 63]] = 0.5
+    kvec[1, [0, 1, 2, 3]] = 0.5
+    t2 = dict(tok, k=np.broadcast_to(f32_to_bf16_bits(kvec), tok["k"].shape).copy(),
+              alpha=np.ones_like(tok["alpha"]), beta=np.ones_like(tok["beta"]))
+    out = prefill(*_dev(t2), S_init=init).cpu().numpy()[0]
+    S_in = init.cpu().numpy()[0].astype(np.float64)
+    v_last = bf16_bits_to_f32(tok["v"][0, L - 1]).astype(np.float64)
+    for h in range(2):
+        kk = kvec[h]
+        want = S_in[h] @ (np.eye(64) - np.outer(kk, kk)) + np.outer(v_last[h], kk)
+        assert np.abs(out[h] - want).max() <= S_TOL, h
+
+    # alpha = 0 at token 20 (inside the second chunk) forgets everything before
+    # it: the fold equals that of tokens 20.. alone, from a zero state
+    t3 = dict(tok, alpha=tok["alpha"].copy())
+    t3["alpha"][:, 20] = 0.0
+    whole = prefill(*_dev(t3), S_init=init)
+    tail = {key: np.ascontiguousarray(val[:, 20:]) for key, val in t3.items()}
+    assert (whole - prefill(*_dev(tail))).abs().max().item() <= 1e-5
+    assert np.abs(whole.cpu().numpy()[0] - _oracle(tail, 0)).max() <= S_TOL
+
+    # gates drawn from {0, 1, ordinary} and keys drawn from three per head
+    # (each also negated) over 100 tokens at d = 128, against the oracle
+    shape = shape_of(0, name="prefill_gates128", H=2, dk=128, dv=128)
+    t4 = _host_tokens(shape, 2, 100)
+    rng = np.random.default_rng(9)
+    pool = t4["k"][:, :3]
+    pick = rng.integers(0, 3, size=t4["k"].shape[:3])
+    n_, L_, H_ = pick.shape
+    keys = pool[np.arange(n_)[:, None, None], pick, np.arange(H_)[None, None, :]]
+    sign = np.where(rng.random(pick.shape) < 0.5, 0, 0x8000).astype(np.uint16)
+    t4["k"] = keys ^ sign[..., None]
+    for key in ("alpha", "beta"):
+        pick = rng.integers(0, 3, size=t4[key].shape)
+        t4[key] = np.where(pick == 0, 0.0, np.where(pick == 1, 1.0, t4[key])).astype(np.float32)
+    print("[prefill] extreme gates d=128 L=100", flush=True)
+    out = prefill(*_dev(t4)).cpu().numpy()
+    for i in range(2):
+        err = np.abs(out[i] - _oracle(t4, i)).max()
+        assert err <= S_TOL, (i, err)
 
 
 def test_prompt_init_equals_float32_init_and_decodes_within_budget():
