@@ -389,8 +389,9 @@ def probe_leg(shape, q, k, S0):
     loop_tflops = n_wg * 8 * iters * 8 * 16384 / t_mfma / 1e12
     R, H, W, dk, dv = shape.R, shape.H, shape.W, shape.dk, shape.dv
     colsum = torch.empty((R * H, dv), dtype=torch.float32, device=q[0].device)
-    t_proj = timed(lambda: probes.projection(S0, k[0], q[0], W, colsum), 20)
-    t_res = timed(lambda: probes.projection(S0, k[0], q[0], W, colsum, resident_pairs=8), 20)
+    pl = probes.planes(S0)                                            # the step kernel's form of S0
+    t_proj = timed(lambda: probes.projection(pl, k[0], q[0], W, colsum), 20)
+    t_res = timed(lambda: probes.projection(pl, k[0], q[0], W, colsum, resident_pairs=8), 20)
     flops = R * H * 2 * W * 2 * dv * dk
     tflops = flops / t_proj / 1e12
     res_tflops = flops / t_res / 1e12
@@ -400,7 +401,8 @@ def probe_leg(shape, q, k, S0):
     return ({"copy_gbs": copy_gbs, "copy_bytes_per_launch": 2 * n * 4, "mfma_loop_tflops": loop_tflops,
              "mfma_loop_frac_of_peak": loop_tflops / BF16_PEAK_TFLOPS},
             {"method": "projection-only probe (onela_probe_projection): the step kernel's 16x16x32 bf16 tiles and "
-                       "split-bf16 S0, k and q staged through LDS 64 beams at a time (next chunk in flight), per-row "
+                       "split-bf16 S0 read from hi/lo planes in A-fragment order (as the step kernel holds it), k and "
+                       "q staged through LDS 64 beams at a time (next chunk in flight), per-row "
                        "sums in place of the replay; all 512 (request, head) pairs, 2W = 512 vectors each. "
                        "'achieved' reads the operands of 8 pairs only (workgroup p reads pair p mod 8), which stay "
                        "in L2: the projection's matrix-core rate; 'full_footprint' streams all 96 MB of operands",

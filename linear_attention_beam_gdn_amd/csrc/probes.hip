@@ -3,11 +3,13 @@
 //
 // copy:        plain 16-byte device copy, the practical HBM rate.
 // mfma loop:   register-only 16x16x32 bf16 MFMAs, the practical matrix-core rate.
+// planes:      S0 to the bf16 hi + lo planes in MFMA A-fragment order, the
+//              form the step kernel holds its shared state in.
 // projection:  P = S0 [k q] for every (request, head) pair with the step
-//              kernel's tiling (wave w holds rows 16w..16w+15 of S0 as hi/lo
-//              bf16 A-fragments; k and q are staged through LDS 64 beams at a
-//              time, the next chunk in flight during this chunk's MFMAs, and
-//              read as B-fragments; two MFMAs per tile), reduced to
+//              kernel's tiling (wave w loads rows 16w..16w+15 of S0 from the
+//              planes as A-fragments; k and q are staged through LDS 64 beams
+//              at a time, the next chunk in flight during this chunk's MFMAs,
+//              and read as B-fragments; two MFMAs per tile), reduced to
 //              per-row sums over the beams so that nothing but the projection
 //              is timed and the result can be checked (S0 times the sum of
 //              the vectors, since the projection is linear).
@@ -58,9 +60,36 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(float* out, int iters) {
     out[(size_t)blockIdx.x * 512 + t] = s;
 }
 
+// fragment f = (w*4 + kk)*64 + lane of a pair's hi plane (then of its lo
+// plane) holds S0[16w + lane%16][32kk + 8(lane/16) + 0..7], d_k = d_v = 128;
+// hi = rne(S0), lo = rne(S0 - hi)
+__global__ __launch_bounds__(256) void planes_kernel(const float* __restrict__ S0, uint16_t* __restrict__ planes,
+                                                     int n_pairs) {
+    constexpr int DK = 128, DV = 128, KS = DK / 32, NFRAG = DV * DK / 8;
+    const int f = blockIdx.x * 256 + threadIdx.x;
+    if (f >= n_pairs * NFRAG) return;
+    const int pr = f / NFRAG, fi = f % NFRAG;
+    const int lane = fi & 63, w = (fi >> 6) / KS, kk = (fi >> 6) % KS;
+    const float* src = S0 + ((size_t)pr * DV + 16 * w + (lane & 15)) * DK + 32 * kk + 8 * (lane >> 4);
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = onela::f32_to_bf16_rne(xv[2 * e]), h1 = onela::f32_to_bf16_rne(xv[2 * e + 1]);
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = onela::f32_to_bf16_rne(xv[2 * e] - __uint_as_float(h0 << 16)) |
+                (onela::f32_to_bf16_rne(xv[2 * e + 1] - __uint_as_float(h1 << 16)) << 16);
+    }
+    u32x4* out = reinterpret_cast<u32x4*>(planes + (size_t)pr * 2 * DV * DK);
+    out[fi] = hi;
+    out[NFRAG + fi] = lo;
+}
+
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void projection_kernel(
-    const float* __restrict__ S0, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q, int H, int W,
-    int resident, float* __restrict__ colsum) {
+    const uint16_t* __restrict__ planes, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q, int H,
+    int W, int resident, float* __restrict__ colsum) {
     constexpr int DK = 128, DV = 128, KS = DK / 32, CH = 64, XS = DK + 16, SEG = DK / 8;
     constexpr int PIECES = (2 * CH * SEG) / 512;     // 16-byte pieces of a chunk per thread
     __shared__ __align__(16) uint16_t xs[2][2 * CH * XS];   // two chunk buffers
@@ -70,23 +99,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void p
     const int n16 = lane & 15, quad = lane >> 4;
 
     bf16x8 a_hi[KS], a_lo[KS];
-    const float* srow = S0 + ((size_t)src * DV + 16 * wave + n16) * DK;
+    {
+        const bf16x8* pl = reinterpret_cast<const bf16x8*>(planes + (size_t)src * 2 * DV * DK);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const float4 x0 = *reinterpret_cast<const float4*>(srow + kk * 32 + quad * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(srow + kk * 32 + quad * 8 + 4);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        u32x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t h0 = onela::f32_to_bf16_rne(xv[2 * e]), h1 = onela::f32_to_bf16_rne(xv[2 * e + 1]);
-            const uint32_t l0 = onela::f32_to_bf16_rne(xv[2 * e] - __uint_as_float(h0 << 16));
-            const uint32_t l1 = onela::f32_to_bf16_rne(xv[2 * e + 1] - __uint_as_float(h1 << 16));
-            hi[e] = h0 | (h1 << 16);
-            lo[e] = l0 | (l1 << 16);
+        for (int kk = 0; kk < KS; ++kk) {
+            a_hi[kk] = pl[(wave * KS + kk) * 64 + lane];
+            a_lo[kk] = pl[DV * DK / 8 + (wave * KS + kk) * 64 + lane];
         }
-        a_hi[kk] = __builtin_bit_cast(bf16x8, hi);
-        a_lo[kk] = __builtin_bit_cast(bf16x8, lo);
     }
 
     const size_t in0 = (size_t)ri * W * H + h;     // input row of (beam 0, head h)
@@ -172,13 +191,21 @@ extern "C" int32_t onela_probe_mfma(float* out, int32_t n_wg, int32_t iters, voi
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-extern "C" int32_t onela_probe_projection(const float* S0, const uint16_t* k, const uint16_t* q, int32_t n_req,
-                                          int32_t H, int32_t W, int32_t resident_pairs, float* colsum,
+extern "C" int32_t onela_probe_planes(const float* S0, uint16_t* planes, int32_t n_pairs, void* hip_stream) {
+    if (!S0 || !planes || n_pairs < 1 || !aligned16(S0) || !aligned16(planes)) return -1;
+    if ((int64_t)n_pairs * 2048 >= INT32_MAX) return -1;
+    hipLaunchKernelGGL(planes_kernel, dim3(n_pairs * 8), dim3(256), 0, static_cast<hipStream_t>(hip_stream), S0,
+                       planes, n_pairs);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int32_t onela_probe_projection(const uint16_t* planes, const uint16_t* k, const uint16_t* q,
+                                          int32_t n_req, int32_t H, int32_t W, int32_t resident_pairs, float* colsum,
                                           void* hip_stream) {
-    if (!S0 || !k || !q || !colsum || n_req < 1 || H < 1 || W < 64 || W % 64 != 0) return -1;
-    if (!aligned16(S0) || !aligned16(k) || !aligned16(q)) return -1;
+    if (!planes || !k || !q || !colsum || n_req < 1 || H < 1 || W < 64 || W % 64 != 0) return -1;
+    if (!aligned16(planes) || !aligned16(k) || !aligned16(q)) return -1;
     if ((int64_t)n_req * H >= INT32_MAX || resident_pairs < 0 || resident_pairs > n_req * H) return -1;
-    hipLaunchKernelGGL(projection_kernel, dim3(n_req * H), dim3(512), 0, static_cast<hipStream_t>(hip_stream), S0, k,
-                       q, H, W, resident_pairs, colsum);
+    hipLaunchKernelGGL(projection_kernel, dim3(n_req * H), dim3(512), 0, static_cast<hipStream_t>(hip_stream),
+                       planes, k, q, H, W, resident_pairs, colsum);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -34,14 +34,15 @@ def test_projection_probe_equals_s0_times_vector_sum():
     ep, S0 = gh.episode(shape)
     W = shape.W
     colsum = torch.empty((shape.R * shape.H, 128), device=gh.dev())
-    probes.projection(gh.to_dev(S0), gh.to_dev(ep["k"][0]), gh.to_dev(ep["q"][0]), W, colsum)
+    pl = probes.planes(gh.to_dev(S0))
+    probes.projection(pl, gh.to_dev(ep["k"][0]), gh.to_dev(ep["q"][0]), W, colsum)
     got = colsum.cpu().numpy().reshape(shape.R, shape.H, 128)
     x = (bf16_bits_to_f32(ep["k"][0]).astype(np.float64) + bf16_bits_to_f32(ep["q"][0])).reshape(shape.R, W, shape.H, 128)
     xs = x.sum(axis=1)                                          # [R][H][dk]
     want = np.einsum("rhij,rhj->rhi", S0.astype(np.float64), xs)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-3)
     # operands of pairs 0 and 1 only: workgroup p reproduces pair p mod 2
-    probes.projection(gh.to_dev(S0), gh.to_dev(ep["k"][0]), gh.to_dev(ep["q"][0]), W, colsum, resident_pairs=2)
+    probes.projection(pl, gh.to_dev(ep["k"][0]), gh.to_dev(ep["q"][0]), W, colsum, resident_pairs=2)
     res = colsum.cpu().numpy()
     flat = got.reshape(-1, 128)
     for p in range(shape.R * shape.H):
