@@ -305,9 +305,9 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
 
     Returns (float32 S0 [R][H][dv][dk] for the comparator or None, prefill record).
     The recurrence itself is 5 d_v d_k flops per token and head (S k, then the
-    decayed rank-one update); the chunked kernel computes it as 16-token
-    products on the matrix cores, whose issued bf16 flops are reported beside
-    it against the bf16 peak.
+    decayed rank-one update); the chunked kernel computes it as products over
+    pairs of 16-token chunks on the matrix cores, whose issued bf16 flops are
+    reported beside it against the bf16 peak.
     """
     import torch
 
@@ -331,11 +331,12 @@ def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     del toks, args
     flops = 5.0 * len(reqs) * prompt_len * shape.H * shape.dv * shape.dk
     tflops = flops / (ms * 1e-3) / 1e12
-    # 16x16x32 products per 16-token chunk and (sequence, head): K K^T (d/32),
-    # and per wave of d/16: P (d/16), Delta (2), update (d/16)
+    # 16x16x32 products per pair of 16-token chunks and (sequence, head): the two
+    # chunks' K K^T and the keys between them (3 x d/32), and per wave of d/16:
+    # P for both chunks (2 d/16), the two solves and the coupling (6), update (2 d/16)
     kc, nw = shape.dk // 16, shape.dv // 16
-    chunks = len(reqs) * shape.H * -(-prompt_len // 16)
-    mfma_flops = chunks * (shape.dk // 32 + nw * (2 * kc + 2)) * 2 * 16 * 16 * 32
+    pairs = len(reqs) * shape.H * -(-prompt_len // 32)
+    mfma_flops = pairs * (3 * (shape.dk // 32) + nw * (4 * kc + 6)) * 2 * 16 * 16 * 32
     mfma_tflops = mfma_flops / (ms * 1e-3) / 1e12
     return S0, {
         "kernel": "prefill_kernel",

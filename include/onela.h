@@ -150,8 +150,8 @@ onela_status onela_init_requests_from_prompts(onela_ctx* ctx, int32_t n_req, con
  * [n_seq][seq_len][H]; S_out device float32 [n_seq][H][d_v][d_k]. S_out may
  * equal S_init (in place). Folding a prompt in two calls (the second starting
  * from the first's S_out) gives bit-identical states to one call when the
- * first call's length is a multiple of 16 tokens (else agreeing to about
- * 1e-5: the prompt is folded in 16-token chunks). Pointers of
+ * first call's length is a multiple of 32 tokens (else agreeing to about
+ * 1e-5: the prompt is folded in pairs of 16-token chunks). Pointers of
  * k, v, S_init, S_out are 16-byte aligned; d_k = d_v in {32, 64, 128}
  * (else ONELA_E_UNSUPPORTED). Asynchronous on hip_stream (NULL = the null
  * stream); errors of the launch itself return ONELA_E_HIP. Allocates nothing. */

@@ -13,17 +13,24 @@
 // i.e. (I + L) Delta = RHS with L_ij = beta_i r_ij (k_i . k_j) (j < i) and
 // RHS_i = beta_i (v_i - g_i S k_i), and the state after the chunk is
 //   S' = g_16 S + sum_j r_16j delta_j k_j^T.
-// T = (I + L)^-1 depends only on the chunk's keys and gates, so it is formed
-// for several chunks at once before the state-dependent part runs. Per chunk
-// the state-dependent part is three small products on the matrix cores:
-//   P = K S^T (16 x d_v), Delta = T RHS, S'^T = g_16 S^T + K^T diag(r_16.) Delta,
-// with the state held as float32 accumulators of S^T (wave w owns columns
+// Chunks are taken in pairs (a, b): over 32 tokens the system is block lower
+// triangular, so with T = (I + L)^-1 of each chunk
+//   Delta_a = T_a RHS_a,
+//   Delta_b = T_b (RHS_b - diag(beta_b g_b) C (r_16a . Delta_a)),  C_ij = k_(b,i) . k_(a,j),
+// where RHS_b uses the decay from the pair's start (g_a16 g_b,i), and
+//   S'' = g_a16 g_b16 S + sum_(j in a) g_b16 r_16j delta_j k_j^T + sum_(j in b) r_16j delta_j k_j^T.
+// T and C depend only on keys and gates, so they are formed for the whole
+// 64-token block before the state-dependent part runs. Per pair that part is a
+// few small products on the matrix cores: P = K S^T for both chunks from one
+// bf16 split of S, the two solves and the coupling, and the state update, with
+// the state held as float32 accumulators of S^T (wave w owns columns
 // [16w, 16w+16) of S^T, i.e. rows of S) and every float32 operand split into
-// bf16 hi + lo (keys are exact in bf16), the hi and lo halves folded into the
-// 32-wide contraction of one 16x16x32 product. The accumulator layout of one
-// product is the operand layout of the next, so nothing is reshuffled between
-// them. A prompt folded in two calls is bit-identical to one call when the first
-// part is a whole number of 16-token chunks.
+// bf16 hi + lo (keys are exact in bf16). The accumulator layout of one product
+// is the operand layout of the next, so nothing is reshuffled between them; the
+// keys are staged in an order that lets one 16-byte LDS read supply an operand
+// spanning two 16-wide tiles (or both chunks of a pair). A prompt folded in two
+// calls is bit-identical to one call when the first part is a whole number of
+// 32-token pairs (a trailing chunk of padding tokens is an exact no-op).
 #include "onela_internal.h"
 
 namespace onela {
@@ -35,7 +42,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSub = 16;        // tokens per chunk (one 16x16x16 MFMA tile)
+constexpr int kSub = 16;        // tokens per chunk (one 16x16 MFMA tile)
 constexpr int kTokBlock = 64;   // tokens staged in LDS at a time
 constexpr int kSubPerBlock = kTokBlock / kSub;
 
@@ -74,29 +81,53 @@ __device__ __forceinline__ s16x8 twice(s16x4 x) { return s16x8{x[0], x[1], x[2],
 
 __device__ __forceinline__ s16x8 cat(s16x4 x, s16x4 y) { return s16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]}; }
 
+// LDS written by some lanes of a wave and then read by others of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Workgroup barrier that orders LDS only, so that global loads in flight (the
+// next token block) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Position of element x (0..31) of a 32-element block in the staged copies: x =
+// 16 h + 4 u + e goes to 8 u + 4 h + e, so that the four values a lane group u
+// takes from the first 16 and the four it takes from the second 16 sit in one
+// 16-byte piece (one LDS read gives an MFMA operand spanning two 16-wide tiles).
+__host__ __device__ constexpr int pair_pos(int x) { return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3); }
+
 template <int DK, int DV, bool PLANES>
 __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void prefill_kernel(const PrefillParams p) {
     constexpr int NW = DV / 16;              // waves; wave w owns state rows [16w, 16w+16)
     constexpr int NT = 64 * NW;
     constexpr int KC = DK / 16;              // 16-wide column tiles of the state
-    constexpr int TB = kTokBlock, NSC = kSubPerBlock;
+    constexpr int TB = kTokBlock, NSC = kSubPerBlock, NSP = NSC / 2;
     constexpr int KR = DK + 8;               // LDS row of a token's key (bf16)
     constexpr int TR = TB + 8;               // LDS row of a key / value column over the block's tokens (bf16)
     constexpr int KP = DK / 8, VP = DV / 8;  // 16-byte pieces per token row
-    static_assert(DK % 16 == 0 && DV % 16 == 0 && 2 * TB <= NT, "prefill block shape");
+    static_assert(DK % 32 == 0 && DV % 16 == 0 && 2 * TB <= NT && NSC % 2 == 0, "prefill block shape");
 
-    __shared__ __align__(16) uint16_t ks[TB * KR];      // keys, token-major
-    __shared__ __align__(16) uint16_t kT[DK * TR];      // keys, column-major
+    __shared__ __align__(16) uint16_t ks[TB * KR];      // keys, token-major, elements in pair_pos order
+    __shared__ __align__(16) uint16_t kT[DK * TR];      // keys, column-major, tokens in pair_pos order
     __shared__ __align__(16) uint16_t vT[DV * TR];      // values, column-major
     __shared__ __align__(16) float as[TB];
     __shared__ __align__(16) float bs[TB];
     __shared__ __align__(16) float Lp[NSC][kSub][4][4];       // L of each chunk: Lp[i][j % 4][j / 4] = L[i][j]
     __shared__ __align__(16) float Ts[NSC][kSub][kSub + 4];   // T = (I + L)^-1
+    __shared__ __align__(16) float Cs[NSP][kSub][kSub + 4];   // k_i . k_j, i in the second chunk of a pair, j in the first
     __shared__ __align__(16) float gs[NSC][kSub];             // g_i
     __shared__ __align__(16) float res[NSC][kSub];            // r_16i
+    // MFMA A-operands in bf16: record [m][i][u] = {hi of row i, columns 4u..4u+3, twice}, {lo, then zeros}
+    __shared__ __align__(16) s16x8 Top[NSC][kSub][4][2];      // T of each chunk
+    __shared__ __align__(16) s16x8 Cop[NSP][kSub][4][2];      // C of each pair
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n16 = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int seq = blockIdx.x / p.H, h = blockIdx.x % p.H;
     const int H = p.H, L = p.L;
     const size_t tok0 = (size_t)seq * L;
@@ -105,6 +136,7 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
     // S^T as accumulators: acc[c][r] = S[16 wave + n16][16 c + 4 q + r]
     f32x4 acc[KC];
     {
+        const int n16 = tid & 15, q = (tid & 63) >> 4;
         const float* si = p.s_init ? p.s_init + state0 + (size_t)(16 * wave + n16) * DK + 4 * q : nullptr;
 #pragma unroll
         for (int c = 0; c < KC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -115,15 +147,24 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
                 acc[c] = f32x4{x.x, x.y, x.z, x.w};
             }
         }
+        // (the initial state is complete before the block loop: otherwise the wait for it,
+        // placed inside the loop, would also wait for the next block's loads every time)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(acc[c]));
     }
 
     // staging: thread (seg, pair) moves 16-byte piece seg of the keys and values of
     // tokens 2 pair and 2 pair + 1, so the column-major copies take 4-byte writes
+    // (every per-lane index below comes from the thread id passed in, an opaque copy
+    // made per block: values derived from it are not hoisted out of the block loop,
+    // where at 128 registers per lane they would be spilled)
     static_assert(NT == (TB / 2) * KP && KP == VP, "one token pair and piece per thread");
-    const int pair = tid % (TB / 2), seg = tid / (TB / 2);
     u32x4 kreg[2], vreg[2];
     float gate = 1.f;
-    auto load_block = [&](int s0) __attribute__((always_inline)) {
+    const float* const alpha_in = p.alpha;
+    const float* const beta_in = p.beta;
+    auto load_block = [&](int s0, int tid) __attribute__((always_inline)) {
+        const int pair = tid % (TB / 2), seg = tid / (TB / 2);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const size_t s = tok0 + min(s0 + 2 * pair + u, L - 1);   // clamped: padding tokens are zeroed below
@@ -132,19 +173,25 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         }
         const int tk = tid % TB;
         const size_t s = tok0 + min(s0 + tk, L - 1);
-        gate = (tid < TB ? p.alpha : p.beta)[s * H + h];           // threads 0..TB-1 alpha, TB..2TB-1 beta
+        gate = (tid < TB ? alpha_in : beta_in)[s * H + h];         // threads 0..TB-1 alpha, TB..2TB-1 beta
     };
-    auto stage_block = [&](int s0) __attribute__((always_inline)) {
+    auto stage_block = [&](int s0, int tid) __attribute__((always_inline)) {
+        const int pair = tid % (TB / 2), seg = tid / (TB / 2);
         const bool in0 = s0 + 2 * pair < L, in1 = s0 + 2 * pair + 1 < L;   // padding tokens: k = v = 0
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         const u32x4 k0 = in0 ? kreg[0] : z, k1 = in1 ? kreg[1] : z;
         const u32x4 v0 = in0 ? vreg[0] : z, v1 = in1 ? vreg[1] : z;
-        *reinterpret_cast<u32x4*>(ks + (2 * pair) * KR + seg * 8) = k0;
-        *reinterpret_cast<u32x4*>(ks + (2 * pair + 1) * KR + seg * 8) = k1;
+        // elements 8 seg .. 8 seg + 7 are two groups of four, each contiguous in pair_pos order
+        const int e0 = pair_pos(8 * seg), e1 = pair_pos(8 * seg + 4);
+        *reinterpret_cast<uint2*>(ks + (2 * pair) * KR + e0) = make_uint2(k0[0], k0[1]);
+        *reinterpret_cast<uint2*>(ks + (2 * pair) * KR + e1) = make_uint2(k0[2], k0[3]);
+        *reinterpret_cast<uint2*>(ks + (2 * pair + 1) * KR + e0) = make_uint2(k1[0], k1[1]);
+        *reinterpret_cast<uint2*>(ks + (2 * pair + 1) * KR + e1) = make_uint2(k1[2], k1[3]);
+        const int tpos = pair_pos(2 * pair);                       // tokens 2 pair, 2 pair + 1 stay adjacent
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e) * TR + 2 * pair) = (k0[e] & 0xffffu) | (k1[e] << 16);
-            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e + 1) * TR + 2 * pair) = (k0[e] >> 16) | (k1[e] & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e) * TR + tpos) = (k0[e] & 0xffffu) | (k1[e] << 16);
+            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e + 1) * TR + tpos) = (k0[e] >> 16) | (k1[e] & 0xffff0000u);
             *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e) * TR + 2 * pair) = (v0[e] & 0xffffu) | (v1[e] << 16);
             *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e + 1) * TR + 2 * pair) = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
         }
@@ -153,16 +200,48 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         else if (tid < 2 * TB) bs[tk] = s0 + tk < L ? gate : 0.f;
     };
 
+    // row i = lane / 4, columns 4u..4u+3 (u = lane % 4) of a 16 x 16 float32 matrix in LDS
+    // (rows of kSub + 4) as the bf16 A-operand record {hi twice}, {lo, zeros}
+    auto write_operand = [&](const float* m, s16x8* dst, int lane) __attribute__((always_inline)) {
+        const float4 x = *reinterpret_cast<const float4*>(m + (lane >> 2) * (kSub + 4) + 4 * (lane & 3));
+        s16x4 hi, lo;
+        split4(f32x4{x.x, x.y, x.z, x.w}, hi, lo);
+        dst[0] = twice(hi);
+        dst[1] = cat(lo, s16x4{0, 0, 0, 0});
+    };
+
     const int nblk = (L + TB - 1) / TB;
-    if (nblk > 0) load_block(0);
+    if (nblk > 0) load_block(0, tid);
     for (int blk = 0; blk < nblk; ++blk) {
         const int s0 = blk * TB;
-        stage_block(s0);
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
+        const int lane = tid_l & 63, n16 = lane & 15, q = lane >> 4;
+        stage_block(s0, tid_l);
         __syncthreads();
-        const int nsub = min(NSC, (L - s0 + kSub - 1) / kSub);
+        const int npair = min(NSP, (L - s0 + 2 * kSub - 1) / (2 * kSub));   // chunk pairs holding prompt tokens
+        const int nsub = 2 * npair;                                         // (a trailing chunk of padding is a no-op)
 
-        // ---- per chunk, state-independent: L, T = (I + L)^-1, g, r_16. ----
-        for (int sc = wave; sc < nsub; sc += NW) {
+        // ---- state-independent part, one task per wave. Tasks 0 .. nsub-1: a chunk's L,
+        // T = (I + L)^-1, g, r_16; tasks nsub .. nsub+npair-1: the key products C between
+        // the two chunks of a pair. T and C leave as bf16 hi/lo MFMA A-operands (Top, Cop) ----
+        for (int task = wave; task < nsub + npair; task += NW) {
+            if (task >= nsub) {
+                // C_ij = k_i . k_j, i in chunk b, j in chunk a of pair sp
+                const int sp = task - nsub, a = 2 * sp, b = a + 1;
+                const uint16_t* kb = ks + (b * kSub + n16) * KR + 8 * q;
+                const uint16_t* ka = ks + (a * kSub + n16) * KR + 8 * q;
+                f32x4 C = f32x4{0.f, 0.f, 0.f, 0.f};                  // C[4q + r][n16]
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk)
+                    C = mfma32(*reinterpret_cast<const s16x8*>(kb + 32 * kk), *reinterpret_cast<const s16x8*>(ka + 32 * kk), C);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Cs[sp][4 * q + r][n16] = C[r];
+                wave_lds_sync();
+                write_operand(&Cs[sp][0][0], Cop[sp][lane >> 2][lane & 3], lane);
+                continue;
+            }
+            const int sc = task;
             const uint16_t* kr8 = ks + (sc * kSub + n16) * KR + 8 * q;
             f32x4 G = f32x4{0.f, 0.f, 0.f, 0.f};                    // G[4q + r][n16] = k_i . k_j
 #pragma unroll
@@ -227,59 +306,93 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
 #pragma unroll
                 for (int k = 0; k < 4; ++k) Ts[sc][4 * k + pp][j] = tp[k];
             }
+            wave_lds_sync();
+            write_operand(&Ts[sc][0][0], Top[sc][lane >> 2][lane & 3], lane);
         }
         __syncthreads();
-        if (blk + 1 < nblk) load_block(s0 + TB);                    // in flight while the chunks are folded
+        if (blk + 1 < nblk) load_block(s0 + TB, tid_l);                    // in flight while the chunks are folded
 
-        // ---- per chunk, in order: the state-dependent part ----
-        for (int sc = 0; sc < nsub; ++sc) {
-            const uint16_t* kr = ks + (sc * kSub + n16) * KR + 4 * q;
-            // P[i][v] = (S k_i)[v] for i = 4q + r, v = 16 wave + n16
-            f32x4 Ph = f32x4{0.f, 0.f, 0.f, 0.f}, Pl = f32x4{0.f, 0.f, 0.f, 0.f};   // even / odd column tiles
+        // ---- per chunk pair (a, b), in order: the state-dependent part.
+        // P = K S^T for both chunks from one split of S; Delta_a = T_a RHS_a;
+        // Delta_b = T_b (RHS_b - diag(beta_b g_b) C (r_16a . Delta_a)) (the 32-token system is
+        // block lower triangular); S^T <- g_a16 g_b16 S^T + K_a^T D_a + K_b^T D_b with
+        // D_a = g_b16 r_16a . Delta_a, D_b = r_16b . Delta_b ----
+        for (int sp = 0; sp < npair; ++sp) {
+            const int a = 2 * sp, b = a + 1;
+            const uint16_t* kra = ks + (a * kSub + n16) * KR + 8 * q;
+            const uint16_t* krb = kra + kSub * KR;
+            // P[i][v] = (S k_i)[v] for i = 4q + r, v = 16 wave + n16; two chains per chunk (hi, lo)
+            f32x4 Xa = f32x4{0.f, 0.f, 0.f, 0.f}, Ya = Xa, Xb = Xa, Yb = Xa;
 #pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                const s16x4 a = *reinterpret_cast<const s16x4*>(kr + 16 * c);
-                s16x4 bh, bl;
-                split4(acc[c], bh, bl);
-                if (c & 1) Pl = mfma32(twice(a), cat(bh, bl), Pl);
-                else Ph = mfma32(twice(a), cat(bh, bl), Ph);
+            for (int cp = 0; cp < KC / 2; ++cp) {
+                s16x4 h0, l0, h1, l1;
+                split4(acc[2 * cp], h0, l0);
+                split4(acc[2 * cp + 1], h1, l1);
+                const s16x8 bh = cat(h0, h1), bl = cat(l0, l1);
+                const s16x8 ka8 = *reinterpret_cast<const s16x8*>(kra + 32 * cp);
+                const s16x8 kb8 = *reinterpret_cast<const s16x8*>(krb + 32 * cp);
+                Xa = mfma32(ka8, bh, Xa);
+                Ya = mfma32(ka8, bl, Ya);
+                Xb = mfma32(kb8, bh, Xb);
+                Yb = mfma32(kb8, bl, Yb);
             }
-            // RHS_i = beta_i (v_i - g_i S k_i)
-            const uint2 vb = *reinterpret_cast<const uint2*>(vT + (16 * wave + n16) * TR + sc * kSub + 4 * q);
-            const float vv[4] = {__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
-                                 __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
-            const float4 bq = *reinterpret_cast<const float4*>(bs + sc * kSub + 4 * q);
-            const float4 gq = *reinterpret_cast<const float4*>(&gs[sc][4 * q]);
-            const float4 rq = *reinterpret_cast<const float4*>(&res[sc][4 * q]);
-            const float bv[4] = {bq.x, bq.y, bq.z, bq.w}, gv[4] = {gq.x, gq.y, gq.z, gq.w};
-            const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
-            f32x4 rhs;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rhs[r] = bv[r] * (vv[r] - gv[r] * (Ph[r] + Pl[r]));
-            // Delta = T RHS (both float32: hi*hi + hi*lo + lo*hi)
-            const float4 tr = *reinterpret_cast<const float4*>(&Ts[sc][n16][4 * q]);
-            s16x4 th, tl, rh, rl;
-            split4(f32x4{tr.x, tr.y, tr.z, tr.w}, th, tl);
-            split4(rhs, rh, rl);
-            f32x4 dl = mfma32(twice(th), cat(rh, rl), f32x4{0.f, 0.f, 0.f, 0.f});   // T_hi (R_hi + R_lo)
-            dl = mfma32(cat(tl, s16x4{0, 0, 0, 0}), cat(rh, rh), dl);                 // + T_lo R_hi
-            // S' = g_16 S + K^T D with D_i = r_16i delta_i
-            const float g16 = gs[sc][kSub - 1];                      // decay over the whole chunk
-            f32x4 dd;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dd[r] = dl[r] * rv[r];
-            s16x4 dh, dlo;
-            split4(dd, dh, dlo);
-            const uint16_t* kc = kT + n16 * TR + sc * kSub + 4 * q;
+            const float4 gaq = *reinterpret_cast<const float4*>(&gs[a][4 * q]);
+            const float4 gbq = *reinterpret_cast<const float4*>(&gs[b][4 * q]);
+            const float4 raq = *reinterpret_cast<const float4*>(&res[a][4 * q]);
+            const float4 rbq = *reinterpret_cast<const float4*>(&res[b][4 * q]);
+            const float4 baq = *reinterpret_cast<const float4*>(bs + a * kSub + 4 * q);
+            const float4 bbq = *reinterpret_cast<const float4*>(bs + b * kSub + 4 * q);
+            const float ga16 = gs[a][kSub - 1], gb16 = gs[b][kSub - 1];
+            const uint2 vab = *reinterpret_cast<const uint2*>(vT + (16 * wave + n16) * TR + a * kSub + 4 * q);
+            const uint2 vbb = *reinterpret_cast<const uint2*>(vT + (16 * wave + n16) * TR + b * kSub + 4 * q);
+            // RHS_a,i = beta_i (v_i - g_i S k_i)
+            const f32x4 rhs_a = f32x4{baq.x * (__uint_as_float(vab.x << 16) - gaq.x * (Xa[0] + Ya[0])),
+                                      baq.y * (__uint_as_float(vab.x & 0xffff0000u) - gaq.y * (Xa[1] + Ya[1])),
+                                      baq.z * (__uint_as_float(vab.y << 16) - gaq.z * (Xa[2] + Ya[2])),
+                                      baq.w * (__uint_as_float(vab.y & 0xffff0000u) - gaq.w * (Xa[3] + Ya[3]))};
+            // RHS_b,i = beta_i (v_i - g_a16 g_i S k_i), before the coupling to chunk a
+            f32x4 rhs_b = f32x4{bbq.x * (__uint_as_float(vbb.x << 16) - ga16 * gbq.x * (Xb[0] + Yb[0])),
+                                bbq.y * (__uint_as_float(vbb.x & 0xffff0000u) - ga16 * gbq.y * (Xb[1] + Yb[1])),
+                                bbq.z * (__uint_as_float(vbb.y << 16) - ga16 * gbq.z * (Xb[2] + Yb[2])),
+                                bbq.w * (__uint_as_float(vbb.y & 0xffff0000u) - ga16 * gbq.w * (Xb[3] + Yb[3]))};
+            // Delta_a = T_a RHS_a (float32 both: hi*hi + hi*lo + lo*hi)
+            s16x4 h, l;
+            split4(rhs_a, h, l);
+            s16x8 bop = cat(h, l);
+            f32x4 da = mfma32(Top[a][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            da = mfma32(Top[a][n16][q][1], bop, da);
+            // RHS_b,i -= beta_i g_i sum_j C_ij r_16j delta_j, then Delta_b = T_b RHS_b
+            const f32x4 xa = f32x4{da[0] * raq.x, da[1] * raq.y, da[2] * raq.z, da[3] * raq.w};
+            split4(xa, h, l);
+            bop = cat(h, l);
+            f32x4 cx = mfma32(Cop[sp][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            cx = mfma32(Cop[sp][n16][q][1], bop, cx);
+            rhs_b[0] = fmaf(-bbq.x * gbq.x, cx[0], rhs_b[0]);
+            rhs_b[1] = fmaf(-bbq.y * gbq.y, cx[1], rhs_b[1]);
+            rhs_b[2] = fmaf(-bbq.z * gbq.z, cx[2], rhs_b[2]);
+            rhs_b[3] = fmaf(-bbq.w * gbq.w, cx[3], rhs_b[3]);
+            split4(rhs_b, h, l);
+            bop = cat(h, l);
+            f32x4 db = mfma32(Top[b][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            db = mfma32(Top[b][n16][q][1], bop, db);
+            // the state update: D_a, D_b as bf16 hi + lo against the keys of both chunks
+            s16x4 dha, dla, dhb, dlb;
+            split4(xa * gb16, dha, dla);
+            split4(f32x4{db[0] * rbq.x, db[1] * rbq.y, db[2] * rbq.z, db[3] * rbq.w}, dhb, dlb);
+            const s16x8 uh = cat(dha, dhb), ul = cat(dla, dlb);
+            const float g32 = ga16 * gb16;                           // decay over the whole pair
+            const uint16_t* kc = kT + n16 * TR + a * kSub + 8 * q;
 #pragma unroll
             for (int t = 0; t < KC; ++t) {
-                const s16x4 a = *reinterpret_cast<const s16x4*>(kc + 16 * t * TR);
-                acc[t] = mfma32(twice(a), cat(dh, dlo), acc[t] * g16);
+                const s16x8 kt8 = *reinterpret_cast<const s16x8*>(kc + 16 * t * TR);
+                acc[t] = mfma32(kt8, uh, acc[t] * g32);
+                acc[t] = mfma32(kt8, ul, acc[t]);
             }
         }
         __syncthreads();                                            // LDS is restaged next
     }
 
+    const int n16 = tid & 15, q = (tid & 63) >> 4;
     const int row = 16 * wave + n16;
     if (!PLANES) {
 #pragma unroll

@@ -66,8 +66,8 @@ def test_prefill_zero_length_and_split_prompts():
     empty = lambda x: x[:, :0].contiguous()
     assert torch.equal(prefill(empty(k), empty(v), empty(a), empty(b), S_init=init), init)
     assert torch.count_nonzero(prefill(empty(k), empty(v), empty(a), empty(b))) == 0
-    # 45 tokens at once == 32 then 13 (in place), bit for bit (the chunks are
-    # the same); a split inside a 16-token chunk (29 + 16) agrees to 1e-5
+    # 45 tokens at once == 32 then 13 (in place), bit for bit (the chunk pairs
+    # are the same); a split inside a pair (29 + 16) agrees to 1e-5
     whole = prefill(k, v, a, b)
     part = lambda x, s: x[:, s].contiguous()
 
