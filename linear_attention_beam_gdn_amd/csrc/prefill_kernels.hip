@@ -88,14 +88,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Workgroup barrier that orders LDS only, so that global loads in flight (the
-// next token block) are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Position of element x (0..31) of a 32-element block in the staged copies: x =
 // 16 h + 4 u + e goes to 8 u + 4 h + e, so that the four values a lane group u
 // takes from the first 16 and the four it takes from the second 16 sit in one
@@ -118,7 +110,8 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
     __shared__ __align__(16) uint16_t vT[DV * TR];      // values, column-major
     __shared__ __align__(16) float as[TB];
     __shared__ __align__(16) float bs[TB];
-    __shared__ __align__(16) float Lp[NSC][kSub][4][4];       // L of each chunk: Lp[i][j % 4][j / 4] = L[i][j]
+    constexpr int LRC = kSub * kSub + 4;     // floats per chunk of Lr
+    __shared__ __align__(16) float Lr[NSC * LRC];             // L of each chunk, row-major
     __shared__ __align__(16) float Ts[NSC][kSub][kSub + 4];   // T = (I + L)^-1
     __shared__ __align__(16) float Cs[NSP][kSub][kSub + 4];   // k_i . k_j, i in the second chunk of a pair, j in the first
     __shared__ __align__(16) float gs[NSC][kSub];             // g_i
@@ -219,92 +212,86 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         const int lane = tid_l & 63, n16 = lane & 15, q = lane >> 4;
         stage_block(s0, tid_l);
         __syncthreads();
-        const int npair = min(NSP, (L - s0 + 2 * kSub - 1) / (2 * kSub));   // chunk pairs holding prompt tokens
-        const int nsub = 2 * npair;                                         // (a trailing chunk of padding is a no-op)
+        // chunk pairs holding prompt tokens (a trailing chunk of padding is an exact no-op)
+        const int npair = min(NSP, (L - s0 + 2 * kSub - 1) / (2 * kSub));
 
-        // ---- state-independent part, one task per wave. Tasks 0 .. nsub-1: a chunk's L,
-        // T = (I + L)^-1, g, r_16; tasks nsub .. nsub+npair-1: the key products C between
-        // the two chunks of a pair. T and C leave as bf16 hi/lo MFMA A-operands (Top, Cop) ----
-        for (int task = wave; task < nsub + npair; task += NW) {
-            if (task >= nsub) {
+        // ---- state-independent part, one task per wave (all chunks of the block are staged,
+        // padding included, so every chunk is formed). Tasks 0 .. NSC-1: a chunk's L, g, r_16
+        // and T = (I + L)^-1; tasks NSC ..: the key products C between the two chunks of a
+        // pair. T and C leave as bf16 hi/lo MFMA A-operands (Top, Cop) ----
+        for (int task = wave; task < NSC + NSP; task += NW) {
+            if (task >= NSC) {
                 // C_ij = k_i . k_j, i in chunk b, j in chunk a of pair sp
-                const int sp = task - nsub, a = 2 * sp, b = a + 1;
+                const int sp = task - NSC, a = 2 * sp, b = a + 1;
                 const uint16_t* kb = ks + (b * kSub + n16) * KR + 8 * q;
                 const uint16_t* ka = ks + (a * kSub + n16) * KR + 8 * q;
-                f32x4 C = f32x4{0.f, 0.f, 0.f, 0.f};                  // C[4q + r][n16]
+                f32x4 C = f32x4{0.f, 0.f, 0.f, 0.f};                // C[4q + e][n16]
 #pragma unroll
                 for (int kk = 0; kk < DK / 32; ++kk)
                     C = mfma32(*reinterpret_cast<const s16x8*>(kb + 32 * kk), *reinterpret_cast<const s16x8*>(ka + 32 * kk), C);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Cs[sp][4 * q + r][n16] = C[r];
+                for (int e = 0; e < 4; ++e) Cs[sp][4 * q + e][n16] = C[e];
                 wave_lds_sync();
                 write_operand(&Cs[sp][0][0], Cop[sp][lane >> 2][lane & 3], lane);
                 continue;
             }
             const int sc = task;
             const uint16_t* kr8 = ks + (sc * kSub + n16) * KR + 8 * q;
-            f32x4 G = f32x4{0.f, 0.f, 0.f, 0.f};                    // G[4q + r][n16] = k_i . k_j
+            f32x4 G = f32x4{0.f, 0.f, 0.f, 0.f};                    // G[4q + e][n16] = k_i . k_j
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const s16x8 a = *reinterpret_cast<const s16x8*>(kr8 + 32 * kk);
                 G = mfma32(a, a, G);
             }
-            float al[kSub], be[4];                                   // the chunk's decays (broadcast reads)
+            // r_ij = alpha_{j+1} ... alpha_i for i = 4q + e, j = n16: the product of
+            // a_m = (m > j ? alpha_m : 1) over m <= i, taken within the lane group
+            // (m = 4q .. 4q+3) and then across the groups below (same column)
+            const float4 a4 = *reinterpret_cast<const float4*>(as + sc * kSub + 4 * q);
+            const float4 b4 = *reinterpret_cast<const float4*>(bs + sc * kSub + 4 * q);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+            float rr[4], run = 1.f;
 #pragma unroll
-            for (int m4 = 0; m4 < kSub / 4; ++m4) {
-                const float4 x = *reinterpret_cast<const float4*>(as + sc * kSub + 4 * m4);
-                al[4 * m4] = x.x; al[4 * m4 + 1] = x.y; al[4 * m4 + 2] = x.z; al[4 * m4 + 3] = x.w;
+            for (int e = 0; e < 4; ++e) {
+                run *= 4 * q + e > n16 ? av[e] : 1.f;
+                rr[e] = run;
             }
-            {
-                const float4 x = *reinterpret_cast<const float4*>(bs + sc * kSub + 4 * q);
-                be[0] = x.x; be[1] = x.y; be[2] = x.z; be[3] = x.w;
-            }
-            // r_ij = alpha_{j+1} ... alpha_i for i = 4q + r, j = n16 (a running product over m > j)
-            float rr[4] = {0.f, 0.f, 0.f, 0.f};
-            {
-                float run = 1.f;
+            float x = run;                                          // inclusive scan of the group totals
+            float y = __shfl_up(x, 16, 64);
+            x = q >= 1 ? x * y : x;
+            y = __shfl_up(x, 32, 64);
+            x = q >= 2 ? x * y : x;
+            y = __shfl_up(x, 16, 64);                               // exclusive: groups below this one
+            const float below = q >= 1 ? y : 1.f;
+            float* lrow = Lr + sc * LRC + 4 * q * kSub + n16;
 #pragma unroll
-                for (int m = 0; m < kSub; ++m) {
-                    run *= m > n16 ? al[m] : 1.f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) rr[r] = m == 4 * q + r ? run : rr[r];
-                }
+            for (int e = 0; e < 4; ++e) {
+                rr[e] *= below;
+                lrow[e * kSub] = n16 < 4 * q + e ? bv[e] * rr[e] * G[e] : 0.f;   // L_ij, j < i
             }
-            // L_ij = beta_i r_ij (k_i . k_j) below the diagonal, stored as Lp[i][j % 4][j / 4]
+            if (n16 == 0) {                                         // g_i = alpha_1 r_i1 (1-based)
+                const float a0 = as[sc * kSub];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * q + r;
-                Lp[sc][i][n16 & 3][n16 >> 2] = n16 < i ? be[r] * rr[r] * G[r] : 0.f;
+                for (int e = 0; e < 4; ++e) gs[sc][4 * q + e] = a0 * rr[e];
             }
-            if (lane < kSub) {                                       // g_i = alpha_1 ... alpha_i, r_16i
-                float g = 1.f, re = 1.f;
-#pragma unroll
-                for (int m = 0; m < kSub; ++m) {
-                    g *= m <= lane ? al[m] : 1.f;
-                    re *= m > lane ? al[m] : 1.f;
-                }
-                gs[sc][lane] = g;
-                res[sc][lane] = re;
-            }
-            // T = (I + L)^-1 by forward substitution, four lanes per column: lane = 4 j + p
-            // holds T[4k + p][j] (k = 0..3) and sums its share of each row, the quad adds up
-            {
-                const int j = lane >> 2, pp = lane & 3;
-                float tp[4] = {0.f, 0.f, 0.f, 0.f};
+            if (q == 3) res[sc][n16] = rr[3];                       // r_16j = r_(16, j)
+            wave_lds_sync();
+            // T by forward substitution, lane j < 16 holding column j
+            if (lane < kSub) {
+                const float* L0 = Lr + sc * LRC;
+                float t[kSub];
 #pragma unroll
                 for (int i = 0; i < kSub; ++i) {
-                    const float4 lr = *reinterpret_cast<const float4*>(&Lp[sc][i][pp][0]);   // L[i][4k + pp]
-                    float sum = lr.x * tp[0];
-                    sum = fmaf(lr.y, tp[1], sum);
-                    sum = fmaf(lr.z, tp[2], sum);
-                    sum = fmaf(lr.w, tp[3], sum);
-                    sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0xB1, 0xF, 0xF, true));
-                    sum += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sum), 0x4E, 0xF, 0xF, true));
-                    const float val = (i == j ? 1.f : 0.f) - sum;
-                    tp[i / 4] = pp == (i & 3) ? val : tp[i / 4];
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int m = 0; m + 1 < i; m += 2) {
+                        s0 = fmaf(L0[i * kSub + m], t[m], s0);
+                        s1 = fmaf(L0[i * kSub + m + 1], t[m + 1], s1);
+                    }
+                    if (i & 1) s0 = fmaf(L0[i * kSub + i - 1], t[i - 1], s0);
+                    t[i] = (i == lane ? 1.f : 0.f) - (s0 + s1);
                 }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) Ts[sc][4 * k + pp][j] = tp[k];
+                for (int i = 0; i < kSub; ++i) Ts[sc][i][lane] = t[i];
             }
             wave_lds_sync();
             write_operand(&Ts[sc][0][0], Top[sc][lane >> 2][lane & 3], lane);
