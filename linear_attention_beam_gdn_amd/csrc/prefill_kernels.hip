@@ -116,9 +116,10 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
     __shared__ __align__(16) float Cs[NSP][kSub][kSub + 4];   // k_i . k_j, i in the second chunk of a pair, j in the first
     __shared__ __align__(16) float gs[NSC][kSub];             // g_i
     __shared__ __align__(16) float res[NSC][kSub];            // r_16i
-    // MFMA A-operands in bf16: record [m][i][u] = {hi of row i, columns 4u..4u+3, twice}, {lo, then zeros}
-    __shared__ __align__(16) s16x8 Top[NSC][kSub][4][2];      // T of each chunk
-    __shared__ __align__(16) s16x8 Cop[NSP][kSub][4][2];      // C of each pair
+    // MFMA A-operands in bf16: [m][0][u][i] = hi of row i, columns 4u..4u+3, twice;
+    // [m][1][u][i] = lo, then zeros (a wave's read of one half is 1 KB in lane order)
+    __shared__ __align__(16) s16x8 Top[NSC][2][4][kSub];      // T of each chunk
+    __shared__ __align__(16) s16x8 Cop[NSP][2][4][kSub];      // C of each pair
 
     const int tid = threadIdx.x, wave = tid >> 6;
     const int seq = blockIdx.x / p.H, h = blockIdx.x % p.H;
@@ -193,14 +194,15 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         else if (tid < 2 * TB) bs[tk] = s0 + tk < L ? gate : 0.f;
     };
 
-    // row i = lane / 4, columns 4u..4u+3 (u = lane % 4) of a 16 x 16 float32 matrix in LDS
-    // (rows of kSub + 4) as the bf16 A-operand record {hi twice}, {lo, zeros}
-    auto write_operand = [&](const float* m, s16x8* dst, int lane) __attribute__((always_inline)) {
-        const float4 x = *reinterpret_cast<const float4*>(m + (lane >> 2) * (kSub + 4) + 4 * (lane & 3));
+    // row i = lane % 16, columns 4u..4u+3 (u = lane / 16) of a 16 x 16 float32 matrix in LDS
+    // (rows of kSub + 4) as the bf16 A-operand records {hi twice}, {lo, zeros}
+    auto write_operand = [&](const float* m, s16x8 (*dst)[4][kSub], int lane) __attribute__((always_inline)) {
+        const int i = lane & 15, u = lane >> 4;
+        const float4 x = *reinterpret_cast<const float4*>(m + i * (kSub + 4) + 4 * u);
         s16x4 hi, lo;
         split4(f32x4{x.x, x.y, x.z, x.w}, hi, lo);
-        dst[0] = twice(hi);
-        dst[1] = cat(lo, s16x4{0, 0, 0, 0});
+        dst[0][u][i] = twice(hi);
+        dst[1][u][i] = cat(lo, s16x4{0, 0, 0, 0});
     };
 
     const int nblk = (L + TB - 1) / TB;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Cs[sp][4 * q + e][n16] = C[e];
                 wave_lds_sync();
-                write_operand(&Cs[sp][0][0], Cop[sp][lane >> 2][lane & 3], lane);
+                write_operand(&Cs[sp][0][0], Cop[sp], lane);
                 continue;
             }
             const int sc = task;
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
                 for (int i = 0; i < kSub; ++i) Ts[sc][i][lane] = t[i];
             }
             wave_lds_sync();
-            write_operand(&Ts[sc][0][0], Top[sc][lane >> 2][lane & 3], lane);
+            write_operand(&Ts[sc][0][0], Top[sc], lane);
         }
         __syncthreads();
         if (blk + 1 < nblk) load_block(s0 + TB, tid_l);                    // in flight while the chunks are folded
@@ -346,22 +348,22 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
             s16x4 h, l;
             split4(rhs_a, h, l);
             s16x8 bop = cat(h, l);
-            f32x4 da = mfma32(Top[a][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
-            da = mfma32(Top[a][n16][q][1], bop, da);
+            f32x4 da = mfma32(Top[a][0][q][n16], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            da = mfma32(Top[a][1][q][n16], bop, da);
             // RHS_b,i -= beta_i g_i sum_j C_ij r_16j delta_j, then Delta_b = T_b RHS_b
             const f32x4 xa = f32x4{da[0] * raq.x, da[1] * raq.y, da[2] * raq.z, da[3] * raq.w};
             split4(xa, h, l);
             bop = cat(h, l);
-            f32x4 cx = mfma32(Cop[sp][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
-            cx = mfma32(Cop[sp][n16][q][1], bop, cx);
+            f32x4 cx = mfma32(Cop[sp][0][q][n16], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            cx = mfma32(Cop[sp][1][q][n16], bop, cx);
             rhs_b[0] = fmaf(-bbq.x * gbq.x, cx[0], rhs_b[0]);
             rhs_b[1] = fmaf(-bbq.y * gbq.y, cx[1], rhs_b[1]);
             rhs_b[2] = fmaf(-bbq.z * gbq.z, cx[2], rhs_b[2]);
             rhs_b[3] = fmaf(-bbq.w * gbq.w, cx[3], rhs_b[3]);
             split4(rhs_b, h, l);
             bop = cat(h, l);
-            f32x4 db = mfma32(Top[b][n16][q][0], bop, f32x4{0.f, 0.f, 0.f, 0.f});
-            db = mfma32(Top[b][n16][q][1], bop, db);
+            f32x4 db = mfma32(Top[b][0][q][n16], bop, f32x4{0.f, 0.f, 0.f, 0.f});
+            db = mfma32(Top[b][1][q][n16], bop, db);
             // the state update: D_a, D_b as bf16 hi + lo against the keys of both chunks
             s16x4 dha, dla, dhb, dlb;
             split4(xa * gb16, dha, dla);
