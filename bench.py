@@ -47,8 +47,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_beam_gdn_amd", "csrc", "one
 # --------------------------------------------------------------- counters
 # Kernels summarised from counter runs of this bench, by a fragment of their names.
 COUNTER_KERNELS = [
-    ("step_kernel<128, 128, false>", "::step_kernel<128, 128, false>"),
-    ("step_kernel<128, 128, true> (raw projections in)", "::step_kernel<128, 128, true>"),
+    ("step_kernel<128, 128, false, *>", "::step_kernel<128, 128, false,"),
+    ("step_kernel<128, 128, true, *> (raw projections in)", "::step_kernel<128, 128, true,"),
     ("prefill_kernel<128, 128, true> (5120-token prompts)", "::prefill_kernel<128, 128, true>"),
     ("projection probe, operands streamed", "projection_kernel"),
     ("projection probe, operands L2-resident", "projection_kernel"),
@@ -66,7 +66,9 @@ def counters_from(dirs, command: str) -> str:
     (GRBM_GUI_ACTIVE per XCD x CUs); bank-conflict share = SQ_LDS_BANK_CONFLICT
     over SQ_LDS_IDX_ACTIVE; wave time waiting / issuing = SQ_WAIT_ANY /
     SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES; instructions per wave from SQ_INSTS_*
-    over SQ_WAVES. The projection probe's dispatches are split in launch order:
+    over SQ_WAVES. A step kernel row takes both instantiations (the first step's,
+    which gathers no records, and the general one). The projection probe's
+    dispatches are split in launch order:
     the bench runs the streamed form first, then the L2-resident one.
     """
     import csv

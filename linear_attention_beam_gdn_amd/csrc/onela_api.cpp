@@ -394,7 +394,9 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
             p.t[i] = ctx->steps[reqs[i0 + i]] + 1;
             p.epoch[i] = ctx->epoch[reqs[i0 + i]];
         }
-        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, p, ctx->stream);
+        bool hist = ctx->graph_mode;                  // (graph mode: the step index is on the device)
+        for (int i = 0; i < n; ++i) hist = hist || p.t[i] > 1;
+        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, hist, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
         if (!ctx->graph_mode)                     // (graph mode: the launch advances the device counters)
             for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;

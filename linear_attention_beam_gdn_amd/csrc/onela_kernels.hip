@@ -124,7 +124,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // FUSED: q, k arrive as raw projections and are L2-normalised per head in
 // phase A (float32, rounded to bf16 before any use, so records hold the keys
 // the step used); alpha and beta arrive raw; o leaves as bf16.
-template <int DK, int DV, bool FUSED>
+// HIST = false: every request of the launch takes its first step (no
+// ancestral records), so no record is gathered; the host launches it only
+// then, outside graph mode.
+template <int DK, int DV, bool FUSED, bool HIST>
 __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
     constexpr int CH = kChunk;
     constexpr int NW = DV / kRowsPerWave;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         return;
     }
     const int H = p.H, W = p.W;
-    const int depth = t - 1;                      // ancestral records per beam
+    const int depth = HIST ? t - 1 : 0;           // ancestral records per beam
     const int b_begin = split * p.beams_per_block;
     const int b_end = min(W, b_begin + p.beams_per_block);
     if (b_begin >= b_end) {
@@ -480,13 +483,13 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 }
             }
         };
-        issue_units(wave);
-
-
-        consume_units(wave);
-        for (int u0 = wave + UPP * NW; u0 < n_units; u0 += UPP * NW) {   // deeper histories
-            issue_units(u0);
-            consume_units(u0);
+        if constexpr (HIST) {
+            issue_units(wave);
+            consume_units(wave);
+            for (int u0 = wave + UPP * NW; u0 < n_units; u0 += UPP * NW) {   // deeper histories
+                issue_units(u0);
+                consume_units(u0);
+            }
         }
         {   // k_t . q_t on the vector units, from LDS
             const int bl = tid_l / TPQ, part = tid_l % TPQ;
@@ -519,7 +522,8 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 for (int u = 0; u < DBD; ++u) {
                     const int j = depth - 1 - u;
                     const int r = (bl < nb && j >= 0) ? anc_s[j * CH + bl] : 0;
-                    dd[u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
+                    if constexpr (HIST) dd[u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
+                    else dd[u2][u] = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
             }
             f32x4 acc[4];                  // tiles: k of beams +0..15, k +16..31, q +0..15, q +16..31
@@ -631,21 +635,25 @@ template <int DK, int DV>
 hipError_t prepare_step_t(int T_max, int W) {
     const size_t lds = step_lds_bytes(DK, DV, T_max, W);
     if (lds <= 65536) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV, false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<DK, DV, true>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void* kernels[] = {reinterpret_cast<const void*>(&step_kernel<DK, DV, false, true>),
+                             reinterpret_cast<const void*>(&step_kernel<DK, DV, true, true>),
+                             reinterpret_cast<const void*>(&step_kernel<DK, DV, false, false>),
+                             reinterpret_cast<const void*>(&step_kernel<DK, DV, true, false>)};
+    for (const void* k : kernels) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DK, int DV>
-hipError_t launch_step_t(bool fused, const StepParams& p, hipStream_t s) {
+hipError_t launch_step_t(bool fused, bool hist, const StepParams& p, hipStream_t s) {
     const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
-    const int nblk = p.n_req * p.H * p.n_splits;
-    if (fused)
-        hipLaunchKernelGGL((step_kernel<DK, DV, true>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
-    else
-        hipLaunchKernelGGL((step_kernel<DK, DV, false>), dim3(nblk), dim3(step_threads<DV>()), lds, s, p);
+    const dim3 grid(p.n_req * p.H * p.n_splits), block(step_threads<DV>());
+    if (fused && hist) hipLaunchKernelGGL((step_kernel<DK, DV, true, true>), grid, block, lds, s, p);
+    else if (fused) hipLaunchKernelGGL((step_kernel<DK, DV, true, false>), grid, block, lds, s, p);
+    else if (hist) hipLaunchKernelGGL((step_kernel<DK, DV, false, true>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((step_kernel<DK, DV, false, false>), grid, block, lds, s, p);
     return hipGetLastError();
 }
 
@@ -693,10 +701,10 @@ hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, 
     return hipGetLastError();
 }
 
-hipError_t launch_step(int dk, int dv, bool fused, const StepParams& p, hipStream_t s) {
-    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, p, s);
-    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, p, s);
-    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, p, s);
+hipError_t launch_step(int dk, int dv, bool fused, bool hist, const StepParams& p, hipStream_t s) {
+    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, hist, p, s);
+    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, hist, p, s);
+    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, hist, p, s);
     return hipErrorInvalidValue;
 }
 

@@ -163,6 +163,12 @@ def test_requests_at_different_depths():
             for t in range(shape.T):
                 assert np.abs(o_hist[i][t][:, h] - ref["o"][t]).max() <= gh.TOL
     lay.close()
+    # requests 1 and 2 took their first step in a launch with a later-step request (the
+    # general kernel); all three starting together take it without record gathers: same bits
+    together = gh.run_episode(shape_of(1, name="mixed_depth", R=3, H=4, T=1), ep, S0)
+    for i in (1, 2):
+        assert np.array_equal(o_hist[i][0], together["o"][0][i * W:(i + 1) * W])
+    together["layer"].close()
 
 
 def test_more_requests_than_one_launch():
