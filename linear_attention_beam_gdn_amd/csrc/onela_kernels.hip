@@ -40,6 +40,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerWave = 16;     // d_v rows per wave (one 16x16x32 MFMA tile row block)
+constexpr int kAncBatch = 8;         // ancestry-row entries copied per round of loads
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -388,8 +389,17 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 p.err[slot] = epoch;
                 par = 0;
             }
+            // the parent's row, kAncBatch entries per round: every load of a round is
+            // issued (from clamped, in-row indices) before any is waited for, and stored
+            // unconditionally (entries past the row land in row depth-1, written last)
             const int* src = anc_prev + par * p.T_max;
-            for (int j = 0; j + 1 < depth; ++j) anc_s[j * CH + tid_l] = src[j];
+            for (int j0 = 0; j0 + 1 < depth; j0 += kAncBatch) {
+                int row[kAncBatch];
+#pragma unroll
+                for (int u = 0; u < kAncBatch; ++u) row[u] = src[min(j0 + u, depth - 2)];
+#pragma unroll
+                for (int u = 0; u < kAncBatch; ++u) anc_s[min(j0 + u, depth - 1) * CH + tid_l] = row[u];
+            }
             anc_s[(depth - 1) * CH + tid_l] = (depth - 1) * W + par;   // parent's own record of step t-1
         }
         if constexpr (FUSED) {
@@ -617,7 +627,13 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
         if (p.write_index && h == 0 && depth > 0) {   // one head of the index owner writes it
             int pb = parin[b];
             pb = (pb < 0 || pb >= W) ? 0 : pb;         // (reported in phase A)
-            for (int j = 0; j + 1 < depth; ++j) anc_next[b * p.T_max + j] = anc_prev[pb * p.T_max + j];
+            for (int j0 = 0; j0 + 1 < depth; j0 += kAncBatch) {   // (as the phase-A copy)
+                int row[kAncBatch];
+#pragma unroll
+                for (int u = 0; u < kAncBatch; ++u) row[u] = anc_prev[pb * p.T_max + min(j0 + u, depth - 2)];
+#pragma unroll
+                for (int u = 0; u < kAncBatch; ++u) anc_next[b * p.T_max + min(j0 + u, depth - 1)] = row[u];
+            }
             anc_next[b * p.T_max + depth - 1] = (depth - 1) * W + pb;
         }
     }
