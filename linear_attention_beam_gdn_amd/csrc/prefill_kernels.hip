@@ -308,6 +308,12 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         // D_a = g_b16 r_16a . Delta_a, D_b = r_16b . Delta_b ----
         for (int sp = 0; sp < npair; ++sp) {
             const int a = 2 * sp, b = a + 1;
+            // The vector ALUs are the bottleneck here and the issue arbiter favours older
+            // waves, so the upper half of the workgroup would fall behind and the lower
+            // half wait for it at the block's barrier: the halves take turns at the higher
+            // priority, one chunk pair each.
+            if ((wave >= NW / 2) != (sp & 1)) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
             const uint16_t* kra = ks + (a * kSub + n16) * KR + 8 * q;
             const uint16_t* krb = kra + kSub * KR;
             // P[i][v] = (S k_i)[v] for i = 4q + r, v = 16 wave + n16; two chains per chunk (hi, lo)
@@ -378,6 +384,7 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
                 acc[t] = mfma32(kt8, ul, acc[t]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();                                            // LDS is restaged next
     }
 
