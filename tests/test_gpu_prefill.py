@@ -59,25 +59,27 @@ def test_prefill_prompt_config():
 
 def test_prefill_zero_length_and_split_prompts():
     shape = shape_of(0, name="prefill_split", H=3, dk=64, dv=64)
-    tok = _host_tokens(shape, 2, 45)
+    L = 100
+    tok = _host_tokens(shape, 2, L)
     k, v, a, b = _dev(tok)
     # no tokens: the initial state (or zero) comes back unchanged
     init = torch.randn((2, 3, 64, 64), device=gh.dev())
     empty = lambda x: x[:, :0].contiguous()
     assert torch.equal(prefill(empty(k), empty(v), empty(a), empty(b), S_init=init), init)
     assert torch.count_nonzero(prefill(empty(k), empty(v), empty(a), empty(b))) == 0
-    # 45 tokens at once == 32 then 13 (in place), bit for bit (the chunk pairs
-    # are the same); a split inside a pair (29 + 16) agrees to 1e-5
+    # 100 tokens at once == 32 then 68, or 64 then 36 (in place), bit for bit (the
+    # 32-token chunk pairs are the same); a split inside a pair (45 + 55) agrees to 1e-5
     whole = prefill(k, v, a, b)
     part = lambda x, s: x[:, s].contiguous()
 
     def two_calls(n1):
         first = prefill(part(k, slice(0, n1)), part(v, slice(0, n1)), part(a, slice(0, n1)), part(b, slice(0, n1)))
-        return prefill(part(k, slice(n1, 45)), part(v, slice(n1, 45)), part(a, slice(n1, 45)),
-                       part(b, slice(n1, 45)), S_init=first, out=first)
+        return prefill(part(k, slice(n1, L)), part(v, slice(n1, L)), part(a, slice(n1, L)),
+                       part(b, slice(n1, L)), S_init=first, out=first)
 
     assert torch.equal(whole, two_calls(32))
-    assert (whole - two_calls(29)).abs().max().item() <= 1e-5
+    assert torch.equal(whole, two_calls(64))
+    assert (whole - two_calls(45)).abs().max().item() <= 1e-5
 
 
 def test_prefill_extreme_gates_and_repeated_keys():
