@@ -35,7 +35,8 @@ def _oracle(tok, i, heads=None):
                         tok["alpha"][i][:, sl], tok["beta"][i][:, sl])
 
 
-@pytest.mark.parametrize("d,L,H,n", [(32, 37, 2, 2), (64, 16, 3, 1), (128, 1, 2, 1), (128, 100, 2, 3)])
+@pytest.mark.parametrize("d,L,H,n", [(32, 37, 2, 2), (64, 16, 3, 1), (128, 1, 2, 1), (128, 100, 2, 3),
+                                     (32, 300, 2, 2), (64, 200, 3, 1)])
 def test_prefill_matches_oracle(d, L, H, n):
     shape = shape_of(0, name=f"prefill_d{d}", H=H, dk=d, dv=d)
     tok = _host_tokens(shape, n, L)
