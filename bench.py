@@ -65,7 +65,9 @@ def counters_from(dirs, command: str) -> str:
     over (GRBM_GUI_ACTIVE per XCD x SIMDs); LDS busy = SQ_LDS_IDX_ACTIVE over
     (GRBM_GUI_ACTIVE per XCD x CUs); bank-conflict share = SQ_LDS_BANK_CONFLICT
     over SQ_LDS_IDX_ACTIVE; wave time waiting / issuing = SQ_WAIT_ANY /
-    SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES; instructions per wave from SQ_INSTS_*
+    SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES; VALU busy (an estimate) = 4 cycles per
+    non-MFMA VALU instruction (SQ_INSTS_VALU - SQ_INSTS_MFMA) over the same SIMD cycles;
+    instructions per wave from SQ_INSTS_*
     over SQ_WAVES. A step kernel row takes both instantiations (the first step's,
     which gathers no records, and the general one). The projection probe's
     dispatches are split in launch order:
@@ -100,10 +102,15 @@ def counters_from(dirs, command: str) -> str:
                         derived.setdefault("mfma_busy", []).append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * agent["Simd_Count"]))
                     if "SQ_LDS_IDX_ACTIVE" in c:
                         derived.setdefault("lds_busy", []).append(c["SQ_LDS_IDX_ACTIVE"] / (g * agent["Cu_Count"]))
+                    if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+                        # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+                        # (SQ_INSTS_VALU counts the MFMA instructions too)
+                        valu = c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]
+                        derived.setdefault("valu_busy", []).append(4.0 * valu / (g * agent["Simd_Count"]))
     if not agent:
         raise SystemExit("no agent information under the counter directories")
     mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
-    head = ("| kernel | dispatches | MFMA busy | LDS busy | LDS bank-conflict share | wave time waiting | "
+    head = ("| kernel | dispatches | MFMA busy | VALU busy (est.) | LDS busy | LDS bank-conflict share | wave time waiting | "
             "wave time issuing | VALU / wave | MFMA / wave | LDS / wave | VMEM rd / wave | VMEM wr / wave | "
             "bf16 MFMA GFLOP / dispatch |")
     lines = [head, "|" + "---|" * (head.count("|") - 1)]
@@ -115,6 +122,7 @@ def counters_from(dirs, command: str) -> str:
         ratio = lambda a, b: c[a] / c[b] if c.get(a) is not None and c.get(b) else float("nan")
         lines.append(
             f"| {label} | {n_disp[label]} | {100 * c.get('mfma_busy', float('nan')):.1f}% | "
+            f"{100 * c.get('valu_busy', float('nan')):.0f}% | "
             f"{100 * c.get('lds_busy', float('nan')):.1f}% | {100 * ratio('SQ_LDS_BANK_CONFLICT', 'SQ_LDS_IDX_ACTIVE'):.1f}% | "
             f"{100 * ratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'):.0f}% | {100 * ratio('SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES'):.0f}% | "
             f"{c.get('SQ_INSTS_VALU', float('nan')) / waves:.0f} | {c.get('SQ_INSTS_MFMA', float('nan')) / waves:.0f} | "
