@@ -161,7 +161,7 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         const int pair = tid % (TB / 2), seg = tid / (TB / 2);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const size_t s = tok0 + min(s0 + 2 * pair + u, L - 1);   // clamped: padding tokens are zeroed below
+            const size_t s = tok0 + min(s0 + 2 * pair + u, L - 1);   // (clamped: padding repeats token L-1)
             kreg[u] = *reinterpret_cast<const u32x4*>(p.k + (s * H + h) * DK + seg * 8);
             vreg[u] = *reinterpret_cast<const u32x4*>(p.v + (s * H + h) * DV + seg * 8);
         }
@@ -171,10 +171,9 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
     };
     auto stage_block = [&](int s0, int tid) __attribute__((always_inline)) {
         const int pair = tid % (TB / 2), seg = tid / (TB / 2);
-        const bool in0 = s0 + 2 * pair < L, in1 = s0 + 2 * pair + 1 < L;   // padding tokens: k = v = 0
-        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-        const u32x4 k0 = in0 ? kreg[0] : z, k1 = in1 ? kreg[1] : z;
-        const u32x4 v0 = in0 ? vreg[0] : z, v1 = in1 ? vreg[1] : z;
+        // padding tokens (past L) carry the last token's k and v: with alpha = 1 and beta = 0
+        // every term they enter is multiplied by their beta or their delta, both 0
+        const u32x4 k0 = kreg[0], k1 = kreg[1], v0 = vreg[0], v1 = vreg[1];
         // elements 8 seg .. 8 seg + 7 are two groups of four, each contiguous in pair_pos order
         const int e0 = pair_pos(8 * seg), e1 = pair_pos(8 * seg + 4);
         *reinterpret_cast<uint2*>(ks + (2 * pair) * KR + e0) = make_uint2(k0[0], k0[1]);
@@ -183,11 +182,11 @@ __global__ __launch_bounds__(prefill_threads<DV>(), DV >= 128 ? 4 : 1) void pref
         *reinterpret_cast<uint2*>(ks + (2 * pair + 1) * KR + e1) = make_uint2(k1[2], k1[3]);
         const int tpos = pair_pos(2 * pair);                       // tokens 2 pair, 2 pair + 1 stay adjacent
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e) * TR + tpos) = (k0[e] & 0xffffu) | (k1[e] << 16);
-            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e + 1) * TR + tpos) = (k0[e] >> 16) | (k1[e] & 0xffff0000u);
-            *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e) * TR + 2 * pair) = (v0[e] & 0xffffu) | (v1[e] << 16);
-            *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e + 1) * TR + 2 * pair) = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) {   // (one byte permute per word: low halves, then high halves)
+            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e) * TR + tpos) = __builtin_amdgcn_perm(k1[e], k0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(kT + (seg * 8 + 2 * e + 1) * TR + tpos) = __builtin_amdgcn_perm(k1[e], k0[e], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e) * TR + 2 * pair) = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(vT + (seg * 8 + 2 * e + 1) * TR + 2 * pair) = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302u);
         }
         const int tk = tid % TB;
         if (tid < TB) as[tk] = s0 + tk < L ? gate : 1.f;           // padding tokens: alpha = 1, beta = 0
