@@ -1,0 +1,93 @@
+"""Host-side accounting of bench.py that the reported roofline rests on: the
+distinct ancestral records a step reads (against a brute-force parent walk),
+the algorithmic bytes per launch (against the byte counts written out by
+hand for a small case), and the counter summary (against synthetic counter
+files with known values). No GPU needed."""
+import csv
+import os
+
+import numpy as np
+import pytest
+
+import bench
+from oracle import ancestry_walk
+from workload import shape_of
+from workload.gen import parents_for
+
+
+def _brute_unique(parents_req, t, W):
+    """Record ids every beam of step t reads, as a set, from the oracle's walk."""
+    if t < 2:
+        return 0
+    return len(set(ancestry_walk(parents_req, t, W).ravel().tolist()))
+
+
+@pytest.mark.parametrize("cfg,W,T", [(0, 8, 3), (1, 64, 5), (4, 128, 7)])
+def test_unique_ancestors_matches_parent_walk(cfg, W, T):
+    shape = shape_of(cfg, W=W, T=T)
+    for r in range(2):
+        par = parents_for(shape, r)
+        for t in range(1, T + 1):
+            assert bench.unique_ancestors(par, t) == _brute_unique(par, t, W), (cfg, r, t)
+
+
+def test_step_bytes_small_case_by_hand():
+    # 1 request, 1 head, d = 32, W = 2, T = 3; both step-2 beams descend from step-1
+    # beam 0, step-3 beams from step-2 beams 0 and 1
+    shape = shape_of(0, R=1, H=1, dk=32, dv=32, W=2, T=3)
+    par = np.array([[-1, -1], [0, 0], [0, 1]], dtype=np.int32)[:, None, :]     # [T][R][W]
+    rec = 4 + 4 * 32 + 2 * 32                                                   # alpha, delta, k
+    s0 = 4 * 32 * 32
+    inputs = 2 * (2 * 32 + 2 * 32 + 2 * 32 + 8)
+    append = 2 * rec
+    o = 2 * 4 * 32
+    b1, b2, b3 = (bench.step_bytes(shape, par, t) for t in (1, 2, 3))
+    assert b1["unique_records"] == 0 and b1["total"] == s0 + inputs + append + o
+    # step 2: one distinct record (step 1, beam 0); ancestry rows 1 entry x 2 beams, read and written
+    assert b2["unique_records"] == 1
+    assert b2["total"] == s0 + inputs + append + o + rec + 2 * 4 * 2
+    # step 3: records (2, 0), (2, 1) and (1, 0)
+    assert b3["unique_records"] == 3
+    assert b3["total"] == s0 + inputs + append + o + 3 * rec + 2 * 4 * 4
+
+
+def _write_counter_run(d, rows, agent):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for disp, name, counters in rows:
+            for cn, cv in counters.items():
+                w.writerow({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": cn, "Counter_Value": cv})
+    with open(os.path.join(d, "run_agent_info.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Simd_Count", "Cu_Count", "Num_Xcc"])
+        w.writeheader()
+        w.writerow({"Name": "gfx950", **agent})
+
+
+def test_counter_summary_arithmetic(tmp_path, monkeypatch):
+    agent = {"Simd_Count": 1024, "Cu_Count": 256, "Num_Xcc": 8}
+    name = "void onela::(anonymous namespace)::step_kernel<128, 128, false, true>(onela::StepParams)"
+    gui = 8 * 1000.0                                  # 1000 cycles per XCD
+    # MFMA busy cycles summed over SIMDs: 25% of 1024 SIMDs x 1000 cycles
+    c1 = {"SQ_WAVES": 100.0, "SQ_WAVE_CYCLES": 1e6, "SQ_WAIT_ANY": 6e5, "SQ_ACTIVE_INST_ANY": 1e5,
+          "GRBM_GUI_ACTIVE": gui}
+    c2 = {"SQ_INSTS_VALU": 2e5 + 1e4, "SQ_INSTS_MFMA": 1e4, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1024 * 1000,
+          "SQ_INSTS_LDS": 5e3, "SQ_INSTS_VMEM_RD": 1e3, "SQ_INSTS_VMEM_WR": 5e2, "SQ_INSTS_SALU": 1.0,
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e6, "GRBM_GUI_ACTIVE": gui}
+    c3 = {"SQ_LDS_BANK_CONFLICT": 2e4, "SQ_LDS_IDX_ACTIVE": 1e5, "SQ_WAVES": 100.0, "GRBM_GUI_ACTIVE": gui}
+    dirs = []
+    for i, c in enumerate((c1, c2, c3)):
+        d = str(tmp_path / f"c{i}")
+        _write_counter_run(d, [(7, name, c)], agent)
+        dirs.append(d)
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "counters.txt"))
+    text = bench.counters_from(dirs, "test")
+    row = next(line for line in text.splitlines() if line.startswith("| step_kernel<128, 128, false, *>"))
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[2] == "25.0%"                        # MFMA busy
+    assert cells[3] == "78%"                          # 4 x 2e5 non-MFMA VALU / (1024 x 1000)
+    assert cells[4] == "39.1%"                        # LDS 1e5 / (256 x 1000)
+    assert cells[5] == "20.0%"                        # bank conflicts 2e4 / 1e5
+    assert cells[6] == "60%" and cells[7] == "10%"    # wait / issue over wave cycles
+    assert cells[8] == "2100"                         # VALU per wave (2.1e5 / 100)
