@@ -884,7 +884,7 @@ def main():
                                     args.traffic_command))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requests and heads would shard across GPUs with no exchange inside a step).", file=sys.stderr)
         sys.exit(2)
 

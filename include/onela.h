@@ -68,7 +68,7 @@ typedef int32_t onela_status;
 #define ONELA_E_PARENT_RANGE  (-4)  /* a parent index was outside [0, W) */
 #define ONELA_E_HIP           (-5)  /* a HIP call failed; see onela_last_error */
 #define ONELA_E_OOM           (-6)  /* device allocation failed in onela_create */
-#define ONELA_E_UNSUPPORTED   (-7)  /* head dims or step count this build has no kernel for */
+#define ONELA_E_UNSUPPORTED   (-7)  /* head dims or step count the library has no kernel for */
 
 /* Fixed shape of one context (one GDN layer). Supported: d_k == d_v in
  * {32, 64, 128}; 1 <= beam_width; 1 <= max_steps <= ONELA_MAX_STEPS;
