@@ -162,6 +162,7 @@ onela_status onela_prefill(int32_t n_seq, int32_t num_heads, int32_t d_k, int32_
 /* One decode step of one GDN layer for n_req requests (OneLA review,
  * "Key claims" and "Scope & Claims", paper Eq. 2-4: records (alpha, delta, k)
  * appended per step, projection replay over the ancestry).
+ *   n_req      1 <= n_req <= max_requests (else ONELA_E_INVALID_ARG).
  *   reqs       host int32 [n_req], distinct initialised request ids; each
  *              request advances its own step counter t (requests may be at
  *              different depths).

@@ -74,6 +74,10 @@ def test_host_misuse_is_rejected_without_side_effects():
     arr1 = (ctypes.c_int32 * 1)(0)
     assert lib.onela_step(lay._ctx, 1, arr1, None, p(k), p(v), p(a), p(b), None, p(o), None) == -1
     assert lib.onela_step(lay._ctx, 1, arr1, p(q), p(k), p(v), p(a), p(b), None, None, None) == -1
+    # no requests, or more than the context holds
+    assert lib.onela_step(lay._ctx, 0, arr1, p(q), p(k), p(v), p(a), p(b), None, p(o), None) == -1
+    arr3 = (ctypes.c_int32 * 3)(0, 1, 0)
+    assert lib.onela_step(lay._ctx, 3, arr3, p(q), p(k), p(v), p(a), p(b), None, p(o), None) == -1
     assert lay.get_step(0) == 0                    # nothing above advanced the request
     # step 1 works, step 2 needs parents
     lay.step([0], q, k, v, a, b, None, o)
