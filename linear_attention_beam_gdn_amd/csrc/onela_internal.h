@@ -9,7 +9,8 @@ namespace onela {
 // Requests one step launch carries in its kernel arguments; onela_step splits
 // larger calls into several launches.
 constexpr int kMaxReqPerLaunch = 64;
-// Beams one workgroup stages at a time (one chunk of the beam loop).
+// Beams one workgroup stages at a time (one chunk of the beam loop); launches
+// without ancestral records use chunks of half that size.
 constexpr int kChunk = 64;
 // Widest beam set that is processed in ancestry order (the order lives in LDS).
 constexpr int kOrderMax = 1024;

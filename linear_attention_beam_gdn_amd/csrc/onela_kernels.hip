@@ -127,18 +127,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // the step used); alpha and beta arrive raw; o leaves as bf16.
 // HIST = false: every request of the launch takes its first step (no
 // ancestral records), so no record is gathered; the host launches it only
-// then, outside graph mode.
+// then, outside graph mode. With nothing to gather, its chunks are half as
+// long: shorter staging and compute phases interleave better between the
+// workgroups that share a CU.
 template <int DK, int DV, bool FUSED, bool HIST>
 __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
-    constexpr int CH = kChunk;
+    constexpr int CH = HIST ? kChunk : kChunk / 2;
     constexpr int NW = DV / kRowsPerWave;
     constexpr int NT = 64 * NW;
     constexpr int KS = DK / 32;        // MFMA k-steps
     constexpr int NG = CH / 32;        // 32-beam groups per chunk
     constexpr int XS = DK + 16;        // padded LDS row (bf16 elements): B-fragment reads free of bank conflicts
     constexpr int MT = CH / 16;        // 16-beam tiles per chunk
-    constexpr int TPQ = NT / CH;       // threads per beam for k_t . q_t
-    constexpr int EQ = DK / TPQ;       // elements per thread there
+    constexpr int TPQ = NT / kChunk;   // threads per beam for k_t . q_t (the same split at both chunk
+    constexpr int EQ = DK / TPQ;       // lengths, so both instantiations round it alike); elements per thread
     static_assert(TPQ >= 1 && EQ % 8 == 0, "k_t . q_t split");
     static_assert((2 * CH * (DK / 8)) % NT == 0 && (CH * (DV / 8)) % NT == 0, "whole stream loads per thread");
     constexpr int DBD = 2;             // depths whose delta gathers are in flight together
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] processing order (W <= kOrderMax)
     int* pos_s = reinterpret_cast<int*>(xs);                        // [Wp] before the beam loop: step t-1 positions
     int* ck_s = pos_s + Wp;                                         // [Wp] before the beam loop: sort keys
-    static_assert(2 * CH * XS * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q staging area");
+    static_assert(!HIST || 2 * CH * XS * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q staging area");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
             }
         }
         {   // k_t . q_t on the vector units, from LDS
-            const int bl = tid_l / TPQ, part = tid_l % TPQ;
+            const int bl = min(tid_l / TPQ, CH - 1), part = tid_l % TPQ;   // (threads past the chunk repeat its last beam)
             const uint16_t* kt_s = xs + bl * XS + part * EQ;
             const uint16_t* qt_s = xs + (CH + bl) * XS + part * EQ;
             float kq = 0.f;
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
                 kq = dot8(*reinterpret_cast<const uint4*>(kt_s + s2 * 8), *reinterpret_cast<const uint4*>(qt_s + s2 * 8), kq);
 #pragma unroll
             for (int m = 1; m < TPQ; m <<= 1) kq += __shfl_xor(kq, m, 64);
-            if (part == 0 && bl < nb) kq_s[bl] = kq;
+            if (part == 0 && tid_l / TPQ < nb) kq_s[bl] = kq;
         }
 
         lds_barrier();   // coef_s / kq_s complete
