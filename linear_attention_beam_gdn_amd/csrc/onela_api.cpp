@@ -394,9 +394,13 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
             p.t[i] = ctx->steps[reqs[i0 + i]] + 1;
             p.epoch[i] = ctx->epoch[reqs[i0 + i]];
         }
-        bool hist = ctx->graph_mode;                  // (graph mode: the step index is on the device)
-        for (int i = 0; i < n; ++i) hist = hist || p.t[i] > 1;
-        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, hist, p, ctx->stream);
+        int n_first = 0;
+        for (int i = 0; i < n; ++i) n_first += p.t[i] == 1;
+        const int mode = ctx->graph_mode ? onela::kStepAny
+                         : n_first == n  ? onela::kStepFirst
+                         : n_first == 0  ? onela::kStepHist
+                                         : onela::kStepAny;
+        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, mode, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
         if (!ctx->graph_mode)                     // (graph mode: the launch advances the device counters)
             for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;

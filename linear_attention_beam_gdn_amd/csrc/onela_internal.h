@@ -124,9 +124,11 @@ hipError_t launch_prefill(int dk, int dv, bool planes, const PrefillParams& p, h
 hipError_t launch_fullstate_step(int dk, int dv, const FullStateParams& p, hipStream_t s);
 hipError_t launch_replay_step(int dk, int dv, const ReplayParams& p, hipStream_t s);
 hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int H, hipStream_t s);
-// hist = false only when every request of the launch takes its first step and the
-// step counters are host-side (no ancestral record exists to gather).
-hipError_t launch_step(int dk, int dv, bool fused, bool hist, const StepParams& p, hipStream_t s);
+// Which step bodies a launch needs: every request at its first step (no
+// ancestral record to gather), none at its first step, or either (graph mode,
+// where the step index is on the device, or requests at mixed depths).
+constexpr int kStepFirst = 0, kStepHist = 1, kStepAny = 2;
+hipError_t launch_step(int dk, int dv, bool fused, int mode, const StepParams& p, hipStream_t s);
 // Set the launch attributes the step kernel needs for this shape (once, before any launch).
 hipError_t prepare_step(int dk, int dv, int T_max, int W);
 // steps[req] = steps_value, epoch[req] = epoch_value (a request restarts).

@@ -29,7 +29,8 @@
 // Variants: in graph mode each request's step index comes from device
 // memory and the last workgroup of the request advances it; the FUSED
 // instantiation takes raw projections (per-head L2 normalisation of q and k,
-// the decay and write-strength gates) and writes o as bf16.
+// the decay and write-strength gates) and writes o as bf16; a request at its
+// first step has no ancestral records and runs a body without the gathers.
 #include "onela_internal.h"
 
 namespace onela {
@@ -125,13 +126,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // FUSED: q, k arrive as raw projections and are L2-normalised per head in
 // phase A (float32, rounded to bf16 before any use, so records hold the keys
 // the step used); alpha and beta arrive raw; o leaves as bf16.
-// HIST = false: every request of the launch takes its first step (no
-// ancestral records), so no record is gathered; the host launches it only
-// then, outside graph mode. With nothing to gather, its chunks are half as
-// long: shorter staging and compute phases interleave better between the
-// workgroups that share a CU.
+// HIST = false: the workgroup's request takes its first step (no ancestral
+// records), so no record is gathered. With nothing to gather, its chunks are
+// half as long: shorter staging and compute phases interleave better between
+// the workgroups that share a CU.
 template <int DK, int DV, bool FUSED, bool HIST>
-__global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
+__device__ __forceinline__ void step_body(const StepParams& p) {
     constexpr int CH = HIST ? kChunk : kChunk / 2;
     constexpr int NW = DV / kRowsPerWave;
     constexpr int NT = 64 * NW;
@@ -642,6 +642,31 @@ __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per
     count_done();
 }
 
+// The workgroup's (request, head, beam range), as step_body derives it.
+__device__ __forceinline__ int step_request(const StepParams& p) {
+    int L = blockIdx.x;
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) L = (L & 7) * (nblk >> 3) + (L >> 3);
+    return L / p.n_splits / p.H;
+}
+
+// MODE kStepFirst: every request of the launch is at its first step;
+// kStepHist: none is; kStepAny: each workgroup takes the body without record
+// gathers when its request is at its first step, which the host cannot know
+// in graph mode (the step index lives on the device). The two bodies in one
+// kernel raise its register pressure, so uniform launches keep their own.
+template <int DK, int DV, bool FUSED, int MODE>
+__global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
+    if constexpr (MODE == kStepAny) {
+        const int ri = step_request(p);
+        const int t = p.dev_steps ? p.dev_steps[p.slot[ri]] + 1 : p.t[ri];
+        if (t <= 1) step_body<DK, DV, FUSED, false>(p);
+        else step_body<DK, DV, FUSED, true>(p);
+    } else {
+        step_body<DK, DV, FUSED, MODE == kStepHist>(p);
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_init_t(const float* S0, uint16_t* planes, int H, hipStream_t s) {
     const int n = H * DV * DK / 8;
@@ -653,10 +678,13 @@ template <int DK, int DV>
 hipError_t prepare_step_t(int T_max, int W) {
     const size_t lds = step_lds_bytes(DK, DV, T_max, W);
     if (lds <= 65536) return hipSuccess;
-    const void* kernels[] = {reinterpret_cast<const void*>(&step_kernel<DK, DV, false, true>),
-                             reinterpret_cast<const void*>(&step_kernel<DK, DV, true, true>),
-                             reinterpret_cast<const void*>(&step_kernel<DK, DV, false, false>),
-                             reinterpret_cast<const void*>(&step_kernel<DK, DV, true, false>)};
+    const void* kernels[] = {
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepFirst>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepHist>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepAny>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepFirst>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepHist>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepAny>)};
     for (const void* k : kernels) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -664,14 +692,19 @@ hipError_t prepare_step_t(int T_max, int W) {
     return hipSuccess;
 }
 
+template <int DK, int DV, bool FUSED>
+void launch_step_mode(int mode, dim3 grid, dim3 block, size_t lds, const StepParams& p, hipStream_t s) {
+    if (mode == kStepFirst) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepFirst>), grid, block, lds, s, p);
+    else if (mode == kStepHist) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepHist>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepAny>), grid, block, lds, s, p);
+}
+
 template <int DK, int DV>
-hipError_t launch_step_t(bool fused, bool hist, const StepParams& p, hipStream_t s) {
+hipError_t launch_step_t(bool fused, int mode, const StepParams& p, hipStream_t s) {
     const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
     const dim3 grid(p.n_req * p.H * p.n_splits), block(step_threads<DV>());
-    if (fused && hist) hipLaunchKernelGGL((step_kernel<DK, DV, true, true>), grid, block, lds, s, p);
-    else if (fused) hipLaunchKernelGGL((step_kernel<DK, DV, true, false>), grid, block, lds, s, p);
-    else if (hist) hipLaunchKernelGGL((step_kernel<DK, DV, false, true>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((step_kernel<DK, DV, false, false>), grid, block, lds, s, p);
+    if (fused) launch_step_mode<DK, DV, true>(mode, grid, block, lds, p, s);
+    else launch_step_mode<DK, DV, false>(mode, grid, block, lds, p, s);
     return hipGetLastError();
 }
 
@@ -719,10 +752,11 @@ hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, 
     return hipGetLastError();
 }
 
-hipError_t launch_step(int dk, int dv, bool fused, bool hist, const StepParams& p, hipStream_t s) {
-    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, hist, p, s);
-    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, hist, p, s);
-    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, hist, p, s);
+hipError_t launch_step(int dk, int dv, bool fused, int mode, const StepParams& p, hipStream_t s) {
+    if (mode != kStepFirst && mode != kStepHist && mode != kStepAny) return hipErrorInvalidValue;
+    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, mode, p, s);
+    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, mode, p, s);
+    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, mode, p, s);
     return hipErrorInvalidValue;
 }
 

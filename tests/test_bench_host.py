@@ -67,7 +67,7 @@ def _write_counter_run(d, rows, agent):
 
 def test_counter_summary_arithmetic(tmp_path, monkeypatch):
     agent = {"Simd_Count": 1024, "Cu_Count": 256, "Num_Xcc": 8}
-    name = "void onela::(anonymous namespace)::step_kernel<128, 128, false, true>(onela::StepParams)"
+    name = "void onela::(anonymous namespace)::step_kernel<128, 128, false, 1>(onela::StepParams)"
     gui = 8 * 1000.0                                  # 1000 cycles per XCD
     # MFMA busy cycles summed over SIMDs: 25% of 1024 SIMDs x 1000 cycles
     c1 = {"SQ_WAVES": 100.0, "SQ_WAVE_CYCLES": 1e6, "SQ_WAIT_ANY": 6e5, "SQ_ACTIVE_INST_ANY": 1e5,
