@@ -197,7 +197,15 @@ def time_episodes(run, stream, episodes: int, T: int, instrumented: int = 10):
         run(evs[i])
     torch.cuda.synchronize()
     per = np.array([[evs[i][t][0].elapsed_time(evs[i][t][1]) for t in range(T)] for i in range(instrumented)]) * 1e3
-    return mean_launch_s, wall / episodes, np.median(per, axis=0)
+    return mean_launch_s, wall / episodes, np.median(per, axis=0), per
+
+
+def depth_stats(per_us: np.ndarray) -> dict:
+    """Median, p10 and p90 per depth (columns) of instrumented launch times in microseconds."""
+    return {"median": [round(float(x), 2) for x in np.median(per_us, axis=0)],
+            "p10": [round(float(x), 2) for x in np.percentile(per_us, 10, axis=0)],
+            "p90": [round(float(x), 2) for x in np.percentile(per_us, 90, axis=0)],
+            "episodes": int(per_us.shape[0])}
 
 
 
@@ -467,7 +475,7 @@ def fused_leg(shape, ep, q, k, v, al, be, par, S0, bytes_t, runs=20):
 
     for _ in range(2):
         episode(None)
-    mean_s, _, us = time_episodes(episode, stream, runs, T)
+    mean_s, _, us, _ = time_episodes(episode, stream, runs, T)
     lay.sync()
     lay.close()
     nbytes = [b["total"] - R * W * H * 2 * shape.dv for b in bytes_t]     # o at 2 B instead of 4
@@ -575,7 +583,7 @@ def replay_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, onela
                 events[t][1].record(stream)
 
     episode(None)
-    mean_s, wall, by_depth = time_episodes(episode, stream, 5, T, instrumented=2)
+    mean_s, wall, by_depth, _ = time_episodes(episode, stream, 5, T, instrumented=2)
     rs.sync()
     rs_mem = rs.memory()
     rs.close()
@@ -684,6 +692,103 @@ def sweep_leg(episodes=2):
     }
 
 
+def latency_leg(episodes=20, warmup=3, flush_mib=512):
+    """Per-step latency of the single-request workloads: tiny (1 x 1 head,
+    d = 32, W = 8, T = 3), r1_h16 W = 256 T = 3, and r1_h16 W = 256 T = 7 with
+    S0 folded on the GPU from a 1024-token synthetic prompt.
+
+    Per depth, median, p10 and p90 over `episodes` episodes with a HIP event
+    pair around each launch, taken twice: warm (caches hold the previous
+    episode's inputs and records) and cold (a `flush_mib` MiB buffer is
+    written, untimed, before every step, which evicts the 256 MB last-level
+    cache and the L2s). Also the mean per launch of back-to-back warm episodes
+    with no event between the launches (an event marker between two kernels
+    costs the GPU a few microseconds, a visible share of launches this short),
+    and the algorithmic bytes per step with the HBM fraction they give.
+    """
+    import torch
+
+    from linear_attention_beam_gdn_amd import Onela
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for cfg in (0, 1, 2):
+        shape = shape_of(cfg)
+        R, H, W, T, dk, dv = shape.R, shape.H, shape.W, shape.T, shape.dk, shape.dv
+        ep = make_episode(shape)
+        up = lambda a: (torch.from_numpy(np.ascontiguousarray(a)).view(torch.int16) if a.dtype == np.uint16
+                        else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+        ins = [[up(ep[key][t]) for key in ("q", "k", "v", "alpha", "beta")] for t in range(T)]
+        par = [None] + [up(ep["parents"][t].astype(np.int32)) for t in range(1, T)]
+        o = torch.empty((R * W, H, dv), dtype=torch.float32, device=dev)
+        lay = Onela(R, H, dk, dv, W, T, stream=stream)
+        reqs = list(range(R))
+        if shape.s0 == "prompt":
+            prompt_s0(lay, shape, shape.prompt_len, reqs, dev, stream, need_f32=False)
+            s0_label = f"prompt-derived on the GPU ({shape.prompt_len} synthetic tokens)"
+        else:
+            for r in reqs:
+                lay.init_request(r, up(ep["S0"][r]))
+            s0_label = f"N(0, {shape.s0_sigma}^2)"
+
+        def episode(events=None, cold=False):
+            for r in reqs:
+                lay.reset(r)
+            for t in range(T):
+                if cold:
+                    flush.fill_(t + 1)                      # untimed: before the event pair
+                if events is not None:
+                    events[t][0].record(stream)
+                lay.step(reqs, *ins[t], par[t], o)
+                if events is not None:
+                    events[t][1].record(stream)
+
+        def instrumented(cold):
+            evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+                   for _ in range(episodes)]
+            for i in range(episodes):
+                episode(evs[i], cold)
+            torch.cuda.synchronize()
+            return np.array([[evs[i][t][0].elapsed_time(evs[i][t][1]) for t in range(T)]
+                             for i in range(episodes)]) * 1e3
+
+        for _ in range(warmup):
+            episode()
+        torch.cuda.synchronize()
+        warm = instrumented(False)
+        cold = instrumented(True)
+        reps = 10 * episodes
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            episode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b_us = e0.elapsed_time(e1) * 1e3 / (reps * T)
+        lay.sync()
+        lay.close()
+        bytes_t = [step_bytes(shape, ep["parents"], t + 1)["total"] for t in range(T)]
+        frac = lambda us: [round(b / (x * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for b, x in zip(bytes_t, us)]
+        ws, cs = depth_stats(warm), depth_stats(cold)
+        res[shape.name] = {
+            "what": f"{R} request x {H} heads, d = {dk}, W = {W}, T = {T}, S0 {s0_label}, parents {shape.parents}",
+            "algorithmic_bytes_by_depth": bytes_t,
+            "cold_us_by_depth": cs,
+            "warm_us_by_depth": ws,
+            "cold_hbm_frac_by_depth": frac(cs["median"]),
+            "warm_hbm_frac_by_depth": frac(ws["median"]),
+            "warm_us_per_step_back_to_back": b2b_us,
+            "warm_beam_steps_per_s_back_to_back": R * W / (b2b_us * 1e-6),
+            "cold_us_per_step_mean_of_medians": float(np.mean(cs["median"])),
+        }
+        del ins, par, o
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def stress_leg(episodes=3):
     """The stress workload: 64 requests x 32 heads, d = 128, W = 1024, T = 7,
     Zipf(1.2) parents (deep shared ancestry), inputs drawn on the GPU for all
@@ -722,7 +827,7 @@ def stress_leg(episodes=3):
                 events[t][1].record(stream)
 
     episode(None)
-    mean_s, wall, by_depth = time_episodes(episode, stream, episodes, T, instrumented=2)
+    mean_s, wall, by_depth, per = time_episodes(episode, stream, episodes, T, instrumented=5)
     lay.sync()
     mem = lay.memory()
     lay.close()
@@ -738,6 +843,9 @@ def stress_leg(episodes=3):
         "beam_steps_per_s": R * W * T / wall,
         "kernel_us_mean": mean_s * 1e6,
         "us_by_depth_instrumented": [round(float(x), 1) for x in by_depth],
+        "us_by_depth_instrumented_stats": depth_stats(per),
+        "hbm_frac_by_depth_instrumented": [round(b["total"] / (x * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                           for b, x in zip(bytes_t, by_depth)],
         "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
         "persistent_state_bytes": mem["s0_bytes"] + mem["record_bytes"] + mem["index_bytes"],
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -805,9 +913,13 @@ def cpu_baseline(shape, ep, n_pairs: int):
     """Oracle (float64 full state per beam) on n_pairs (request, head) pairs, all steps."""
     import multiprocessing as mp
 
+    visible = len(os.sched_getaffinity(0))
+    # every host core this process may run on, unless the environment sets a
+    # smaller CPU share (OMP_NUM_THREADS, the per-GPU share on shared hosts)
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    cores = max(1, min(visible, int(share)) if share.isdigit() and int(share) > 0 else visible)
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
-        os.environ[var] = "1"
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        os.environ[var] = "1"                     # one BLAS thread per worker
     rng = np.random.default_rng(7)
     pairs = [(int(rng.integers(shape.R)), int(rng.integers(shape.H))) for _ in range(n_pairs)]
     W = shape.W
@@ -832,17 +944,31 @@ def cpu_baseline(shape, ep, n_pairs: int):
                    f"per beam, from a drawn S0 (the oracle's cost does not depend on S0's values); "
                    f"{wall:.1f} s wall, {sum(per_pair):.1f} s CPU; scaled by {shape.H} heads per beam-step"),
         "cpu_model": _cpu_model(),
+        "host_cpus_visible": visible,
+        "workers": min(cores, n_pairs),
+        "worker_rule": "len(os.sched_getaffinity(0)), capped by OMP_NUM_THREADS when the environment sets it "
+                       "(the host's CPU share per GPU); BLAS threads 1 per worker",
     }
 
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, family/model/stepping, sockets."""
+    fields, sockets = {}, set()
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                continue
+            key, val = (x.strip() for x in line.split(":", 1))
+            if key == "physical id":
+                sockets.add(val)
+            elif key in ("model name", "cpu family", "model", "stepping", "vendor_id") and key not in fields:
+                fields[key] = val
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    return (f"{name} (vendor {fields.get('vendor_id', '?')}, family {fields.get('cpu family', '?')}, "
+            f"model {fields.get('model', '?')}, stepping {fields.get('stepping', '?')}, "
+            f"{max(1, len(sockets))} socket(s))")
 
 
 # ------------------------------------------------------------------- main
@@ -865,6 +991,8 @@ def main():
                     help="skip the operator sweep (OneLA vs both comparators over 24 shapes)")
     ap.add_argument("--no-stress", action="store_true",
                     help="skip the stress-workload leg (64 requests x 32 heads, W = 1024, T = 7)")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the single-request latency leg (tiny, W = 256 T = 3, W = 256 T = 7 prompt-derived)")
     ap.add_argument("--layers", type=int, default=4,
                     help="layers of the multi-layer decode-step leg (eager vs HIP graph); 0 skips it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -952,7 +1080,8 @@ def main():
 
     # Timed region: args.steps episodes back to back, bracketed by
     # synchronisations and one pair of HIP events on the launch stream.
-    mean_launch_s, wall_per_episode, med_t_us = time_episodes(episode, stream, args.steps, T)
+    mean_launch_s, wall_per_episode, med_t_us, per_t_us = time_episodes(episode, stream, args.steps, T,
+                                                                        instrumented=20)
     lay.sync()
 
     bytes_t = [step_bytes(shape, ep["parents"], t + 1) for t in range(T)]
@@ -977,6 +1106,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "precision": ("inputs q, k, v bf16; alpha, beta float32; S0 held as two bf16 planes hi + lo "
+                      "(hi = rne(S0), lo = rne(S0 - hi): about 16 significant bits, ~2^-17 relative); "
+                      "projection bf16 x bf16 products accumulated in float32 on the matrix cores; "
+                      "replay, delta and o in float32; delta records float32"),
         "config": {
             "workload": shape.name,
             "requests": R, "heads": H, "d_k": dk, "d_v": dv, "beam_width": W, "decode_steps": T,
@@ -986,6 +1119,7 @@ def main():
         },
         "us_per_decode_step": ms_per_step * 1e3 / T,
         "us_by_depth_instrumented": [round(float(x), 2) for x in med_t_us],
+        "us_by_depth_instrumented_stats": depth_stats(per_t_us),
         "kernel_us_mean": mean_launch_s * 1e6,
         "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
         "roofline": {
@@ -1007,6 +1141,22 @@ def main():
         out["mfma_projection"]["in_fused_step"] = {
             "achieved_tflops": proj_tflops, "frac": proj_tflops / BF16_PEAK_TFLOPS,
             "note": "the projection's flops over the whole fused launch, which HBM bounds"}
+        mp = out["mfma_projection"]
+        out["roofline_mfma"] = {
+            "bound": "mfma", "kernel": "S0 [k q] projection phase of step_kernel",
+            "achieved": mp["achieved_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": mp["frac"],
+            "issued_frac": mp["issued_frac"],
+            "flops": "algorithmic: 4 W d_v d_k per (request, head); issued counts the hi and lo MFMA of every "
+                     "product (2x)",
+            "method": "projection-only probe with the step kernel's tiles and S0 planes, operands of 8 pairs "
+                      "resident in L2",
+            "streamed_frac": mp["full_footprint"]["frac"],
+            "in_fused_step_frac": proj_tflops / BF16_PEAK_TFLOPS,
+            "hbm_cap_frac": mp["hbm_cap_frac"],
+            "target_frac": 0.4,
+            "target_met_algorithmic": mp["frac"] >= 0.4,
+        }
     if prefill_out is not None:
         out["prefill"] = prefill_out
     mem = lay.memory()
@@ -1025,6 +1175,8 @@ def main():
         out["replay_comparator"] = replay_leg(shape, q, k, v, al, be, par, o,
                                               up(ep["S0"]) if S0_dev is None else S0_dev, stream,
                                               mean_launch_s, ms_per_step, mem)
+    if not args.no_latency:
+        out["latency_configs"] = latency_leg()
     if not args.no_stress:
         out["stress_workload"] = stress_leg()
     if not args.no_sweep:

@@ -87,7 +87,12 @@ typedef struct onela_config {
 
 typedef struct onela_ctx onela_ctx;
 
-/* Create a context on the current HIP device. hip_stream is a hipStream_t
+/* Create a context (one GDN layer) on the current HIP device. It holds what
+ * the method keeps per request (OneLA abstract, readsearch.ai page: one
+ * shared prompt-derived state per request, append-only transition records,
+ * a lightweight ancestry index; OneLA review, evolve.pub, "Summary": the
+ * persistent state is the shared state plus the records), allocated here
+ * once for the largest episode. hip_stream is a hipStream_t
  * (NULL = the null stream). Allocates S0 planes (4*H*d_v*d_k bytes per
  * request), the record store ((4 + 4*d_v + 2*d_k) bytes per record,
  * max_requests*H*max_steps*W records), the ancestry index
@@ -181,8 +186,10 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
                         const float* alpha, const float* beta,
                         const int32_t* parent_idx, float* o, float* delta_out);
 
-/* Rewind request `req` to step 0, keeping its S0 (the records of the old
- * episode become dead and are overwritten by the next one). Host-only and
+/* Rewind request `req` to step 0, keeping its S0 (OneLA abstract: the
+ * shared state is fixed by the prompt, and records are only ever appended, so
+ * a new episode needs no copy of anything: the records of the old episode
+ * become dead and are overwritten by the next one). Host-only and
  * O(1): nothing is enqueued; a device error left by the old episode no
  * longer counts. */
 onela_status onela_reset(onela_ctx* ctx, int32_t req);

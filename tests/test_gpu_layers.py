@@ -1,10 +1,12 @@
 """Several GDN layers of the same requests sharing one ancestry index.
 
-One context owns the index and writes it; the others read it. Each layer's
-outputs must equal those of an independent context on the same inputs, bit
-for bit (same kernels, same index contents), including requests that join at
-different decode steps; the ordering rules of a shared index are enforced on
-the host.
+One context owns the index and writes it; the others read it. Every step,
+layer and head is compared with the float64 oracle (o and delta within 1e-3;
+each layer's ancestry rows equal to a brute-force walk of the parents), and
+each layer's outputs must also equal those of an independent context on the
+same inputs, bit for bit (same kernels, same index contents), including
+requests that join at different decode steps; the ordering rules of a shared
+index are enforced on the host.
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import gpu_harness as gh
     from linear_attention_beam_gdn_amd import Onela, OnelaError
+    from oracle import ancestry_walk
     from workload import shape_of
 
 # (heads, head dim) of the three layers; the owner is layer 0
@@ -54,17 +57,28 @@ def test_shared_index_layers_equal_independent_layers():
         for i in range(n):
             lay.init_request(i, gh.to_dev(S0[i]))
     outs = [[] for _ in layers]
+    deltas = [[] for _ in layers]
     for t in range(eps[0][0].T):
         for li, (lay, (shape, ep, S0)) in enumerate(zip(layers, eps)):
             par = gh.to_dev(ep["parents"][t].astype(np.int32)) if t else None
-            o = torch.empty((n * shape.W, shape.H, shape.dv), dtype=torch.float32, device=gh.dev())
-            lay.step(list(range(n)), *[gh.to_dev(ep[key][t]) for key in ("q", "k", "v", "alpha", "beta")], par, o)
+            o = torch.full((n * shape.W, shape.H, shape.dv), float("nan"), dtype=torch.float32, device=gh.dev())
+            d = torch.full_like(o, float("nan"))
+            lay.step(list(range(n)), *[gh.to_dev(ep[key][t]) for key in ("q", "k", "v", "alpha", "beta")], par, o, d)
             outs[li].append(o)
+            deltas[li].append(d)
     for li, (lay, (shape, ep, S0)) in enumerate(zip(layers, eps)):
         lay.sync()
+        W, T = shape.W, shape.T
+        o_np = [o.cpu().numpy() for o in outs[li]]
+        d_np = [d.cpu().numpy() for d in deltas[li]]
+        for i in range(n):             # every step, head and request against the oracle
+            gh.check_request_steps(shape, ep, S0, i, [o[i * W:(i + 1) * W] for o in o_np],
+                                   [d[i * W:(i + 1) * W] for d in d_np])
+            np.testing.assert_array_equal(lay.get_ancestry(i)[:, :T - 1],
+                                          ancestry_walk(ep["parents"][:, i, :], T, W))
         ref = gh.run_episode(shape, ep, S0)
         for t in range(shape.T):
-            assert np.array_equal(outs[li][t].cpu().numpy(), ref["o"][t]), (li, t)
+            assert np.array_equal(o_np[t], ref["o"][t]), (li, t)
         for i in range(n):
             assert np.array_equal(lay.get_ancestry(i), ref["anc"][-1][i])
         ref["layer"].close()
@@ -100,6 +114,10 @@ def test_shared_index_requests_joining_at_different_steps():
             for j, i in enumerate(active):
                 hist[li][i].append(on[j * W:(j + 1) * W])
     for li, (shape, ep, S0) in enumerate(eps):
+        for i in range(2):             # every step and head of both requests against the oracle
+            gh.check_request_steps(shape, ep, S0, i, hist[li][i])
+            np.testing.assert_array_equal(layers[li].get_ancestry(slots[i])[:, :T - 1],
+                                          ancestry_walk(ep["parents"][:, i, :], T, W))
         ref = gh.run_episode(shape, ep, S0)
         for i in range(2):
             for t in range(T):

@@ -44,6 +44,7 @@ def test_prefill_matches_oracle(d, L, H, n):
     out = prefill(*_dev(tok)).cpu().numpy()
     for i in range(n):
         err = np.abs(out[i] - _oracle(tok, i)).max()
+        gh.parity_log.record("S", err, S_TOL)
         assert err <= S_TOL, (i, err)
 
 
@@ -55,6 +56,7 @@ def test_prefill_prompt_config():
     out = prefill(*_dev(tok)).cpu().numpy()
     err = np.abs(out[0] - _oracle(tok, 0)).max()
     print(f"[prefill] {shape.name}: max-abs err {err:.3e}")
+    gh.parity_log.record("S", err, S_TOL)
     assert err <= S_TOL
 
 
@@ -140,6 +142,7 @@ def test_prefill_extreme_gates_and_repeated_keys():
     out = prefill(*_dev(t4)).cpu().numpy()
     for i in range(2):
         err = np.abs(out[i] - _oracle(t4, i)).max()
+        gh.parity_log.record("S", err, S_TOL)
         assert err <= S_TOL, (i, err)
 
 
@@ -185,6 +188,7 @@ def test_prefill_bench_size_sampled():
         want = _oracle(host, 0)[0]
         err = np.abs(out[r, h].cpu().numpy() - want).max()
         print(f"[prefill] pair ({r}, {h}): max-abs err {err:.3e}", flush=True)
+        gh.parity_log.record("S", err, S_TOL)
         assert err <= S_TOL
 
 

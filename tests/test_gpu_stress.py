@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
+
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
@@ -34,6 +36,8 @@ def test_stress_r64_h32_w1024_t7_sampled():
     o = torch.empty((R * W, H, d), dtype=torch.float32, device=dev)
     dl = torch.empty_like(o)
     for t in range(T):
+        o.fill_(float("nan"))          # a skipped write would stay NaN
+        dl.fill_(float("nan"))
         inp = step_inputs(shape, t, dev)
         par = torch.from_numpy(parents[t].astype(np.int32)).to(dev) if t else None
         lay.step(list(range(R)), inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], par, o, dl)
@@ -62,4 +66,6 @@ def test_stress_r64_h32_w1024_t7_sampled():
         eo = float(np.abs(np.stack(kp["o"]) - ref["o"]).max())
         ed = float(np.abs(np.stack(kp["delta"]) - ref["delta"]).max())
         print(f"[stress] pair {(r, h)}: max-abs err o={eo:.3e} delta={ed:.3e}", flush=True)
+        parity_log.record("o", eo, TOL)
+        parity_log.record("delta", ed, TOL)
         assert eo <= TOL and ed <= TOL
