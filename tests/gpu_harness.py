@@ -118,6 +118,11 @@ def check_request_steps(shape, ep, S0, i, o_req, d_req=None, tol=TOL, heads=None
     return worst
 
 
+def episode(shape, reqs=None):
+    ep = make_episode(shape, reqs=reqs)
+    return ep, s0_for(shape, ep, ep["reqs"])
+
+
 def oracle_refs(shape, ep, S0, pairs):
     """Oracle episodes of the listed (call-local request, head) pairs."""
     return {(i, h): oracle_pair(shape, ep, S0, i, h) for (i, h) in pairs}
