@@ -318,6 +318,129 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, command
     return text
 
 
+def _counter_rows(d):
+    """{(dispatch id, kernel name): {counter: value}} of one rocprofv3 --pmc output directory."""
+    import csv
+    import glob
+
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return rows
+
+
+def profile_by_depth(leg: str, fetch_dir: str, write_dir: str, counter_dirs, copy_mib: int, command: str) -> str:
+    """Per-depth HBM traffic and counters of step_kernel in a run of one bench
+    leg alone (`bench.py --only stress` or `--only multi_layer` under
+    rocprofv3 --pmc): FETCH_SIZE and WRITE_SIZE scaled by the same counters on
+    a plain copy of copy_mib MiB in the same run, set against the algorithmic
+    bytes of each depth from the realised parents; the other counter runs give
+    wave waiting, L1-to-L2 read requests and MFMA / LDS activity per depth.
+    Writes profiles/<kernel>_<workload>_by_depth.txt and returns its text."""
+    if leg == "stress":
+        from workload.gen_device import all_parents
+
+        shape = shape_of(4)
+        parents = all_parents(shape)
+        per_step = 1                                  # launches per decode step
+        fname = "step_kernel_r64_h32_w1024_t7_zipf_by_depth.txt"
+        what = "stress workload r64_h32_d128_w1024_t7, Zipf(1.2) parents"
+    elif leg == "multi_layer":
+        shape = shape_of(3)
+        parents = make_episode(shape, with_s0=False)["parents"]
+        per_step = 4
+        fname = "step_kernel_4layers_r32_h16_w256_t5_by_depth.txt"
+        what = ("4 GDN layers of r32_h16_d128_w256_t5 sharing one ancestry index, eager and graph-replayed "
+                "decode steps (each layer-step is one launch)")
+    else:
+        raise SystemExit(f"no per-depth profile for leg {leg!r}")
+    T = shape.T
+    known = copy_mib * 2.0 ** 20
+
+    def step_disp(rows, counter):
+        step = [c[counter] for (i, n), c in sorted(rows.items()) if f"::{KERNEL_NAME}<" in n and counter in c]
+        copy = [c[counter] for (i, n), c in sorted(rows.items()) if "copyBuffer" in n and counter in c]
+        return step, copy
+
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    fetch, fcopy = step_disp(fr, "FETCH_SIZE")
+    write, wcopy = step_disp(wr, "WRITE_SIZE")
+    if not fetch or not write or not fcopy or not wcopy:
+        raise SystemExit("missing step_kernel or copy dispatches in the FETCH_SIZE / WRITE_SIZE runs")
+    f_scale, w_scale = known / (max(fcopy) * 1024.0), known / (max(wcopy) * 1024.0)
+    depth_of = lambda i: (i // per_step) % T
+    alg = [step_bytes(shape, parents, t + 1)["total"] for t in range(T)]
+    byd = {t: {"fetch": [], "write": []} for t in range(T)}
+    for i, x in enumerate(fetch):
+        byd[depth_of(i)]["fetch"].append(x * 1024.0 * f_scale)
+    for i, x in enumerate(write):
+        byd[depth_of(i)]["write"].append(x * 1024.0 * w_scale)
+    import csv
+    import glob
+
+    agent = {}
+    for d in counter_dirs or []:
+        for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Name", "").startswith("gfx"):
+                    agent = {k: int(r[k]) for k in ("Simd_Count", "Cu_Count", "Num_Xcc")}
+    cnt = {t: {} for t in range(T)}
+    for d in counter_dirs or []:
+        rows = _counter_rows(d)
+        disp = [c for (i, n), c in sorted(rows.items()) if f"::{KERNEL_NAME}<" in n]
+        for i, c in enumerate(disp):
+            for k, v in c.items():
+                cnt[depth_of(i)].setdefault(k, []).append(v)
+            if "GRBM_GUI_ACTIVE" in c and agent:
+                g = c["GRBM_GUI_ACTIVE"] / agent["Num_Xcc"]            # kernel cycles per XCD
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                    cnt[depth_of(i)].setdefault("mfma_busy", []).append(
+                        c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * agent["Simd_Count"]))
+                if "SQ_LDS_IDX_ACTIVE" in c:
+                    cnt[depth_of(i)].setdefault("lds_busy", []).append(c["SQ_LDS_IDX_ACTIVE"] / (g * agent["Cu_Count"]))
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    head = ("| depth | launches | fetch MB | write MB | HBM MB (counters) | algorithmic MB | counters / algorithmic | "
+            "wave time waiting | L1->L2 read requests (M) | MFMA busy | LDS busy |")
+    lines = [head, "|" + "---|" * (head.count("|") - 1)]
+    tot_c = tot_a = 0.0
+    for t in range(T):
+        f, w = mean(byd[t]["fetch"]), mean(byd[t]["write"])
+        c = {k: mean(v) for k, v in cnt[t].items()}
+        ratio = lambda a, b: c[a] / c[b] if c.get(a) is not None and c.get(b) else float("nan")
+        tot_c += f + w
+        tot_a += alg[t]
+        lines.append(f"| {t + 1} | {len(byd[t]['fetch'])} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} | "
+                     f"{alg[t] / 1e6:.1f} | {(f + w) / alg[t]:.3f} | {100 * ratio('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES'):.0f}% | "
+                     f"{c.get('TCP_TCC_READ_REQ_sum', c.get('TCP_TCC_READ_REQ', float('nan'))) / 1e6:.1f} | "
+                     f"{100 * c.get('mfma_busy', float('nan')):.1f}% | {100 * c.get('lds_busy', float('nan')):.1f}% |")
+    text = "\n".join([
+        f"# step_kernel per depth: {what}",
+        "# HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (rocprofv3 --pmc, KiB per dispatch), each scaled",
+        "# by known bytes / counted bytes of one plain device copy in the same run; algorithmic bytes per launch",
+        "# as the bench counts them (distinct ancestral records from the realised parents). Wave time waiting =",
+        "# SQ_WAIT_ANY / SQ_WAVE_CYCLES; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' cycles, LDS busy =",
+        "# SQ_LDS_IDX_ACTIVE over the CUs' cycles (GRBM_GUI_ACTIVE per XCD); L1->L2 read requests =",
+        "# TCP_TCC_READ_REQ summed over the chip. FETCH_SIZE counts L2 fetches from the fabric, which the",
+        "# 256 MB last-level cache may serve before HBM.",
+        f"# commands: {command}",
+        f"kernel_source_sha = {kernel_source_sha()}",
+        f"copy_probe_bytes = {known:.0f}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"hbm_bytes_per_launch_mean = {tot_c / T:.0f}",
+        f"algorithmic_bytes_per_launch_mean = {tot_a / T:.0f}",
+        f"counters_over_algorithmic = {tot_c / tot_a:.4f}",
+        "",
+        *lines,
+        "",
+    ])
+    path = os.path.join(ROOT, "profiles", fname)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write(text)
+    return text
+
+
 def prompt_s0(lay, shape, prompt_len, reqs, dev, stream, need_f32):
     """Fold a synthetic prompt per request into the layer's S0 on the GPU and time it.
 
@@ -1003,6 +1126,11 @@ def main():
     ap.add_argument("--counters-from", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc runs of this bench into the counters file and exit")
     ap.add_argument("--counters-command", default="", help="commands recorded in the counters file")
+    ap.add_argument("--only", choices=("stress", "multi_layer"),
+                    help="run this leg alone (after the copy probe) and print its JSON, for per-depth profiles")
+    ap.add_argument("--profile-by-depth", nargs="+", metavar="DIR",
+                    help="with --only LEG: FETCH_DIR WRITE_DIR [COUNTER_DIR ...] of rocprofv3 --pmc runs of that leg "
+                         "alone; write its per-depth traffic and counter summary under profiles/ and exit")
     args = ap.parse_args()
     if args.counters_from:
         print(counters_from(args.counters_from, args.counters_command))
@@ -1010,6 +1138,12 @@ def main():
     if args.traffic_from:
         print(traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.copy_probe or 256,
                                     args.traffic_command))
+        return
+    if args.profile_by_depth:
+        if not args.only or len(args.profile_by_depth) < 2:
+            raise SystemExit("--profile-by-depth needs --only LEG and at least FETCH_DIR WRITE_DIR")
+        print(profile_by_depth(args.only, args.profile_by_depth[0], args.profile_by_depth[1],
+                               args.profile_by_depth[2:], args.copy_probe or 256, args.counters_command))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -1027,6 +1161,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only == "stress":
+        print(json.dumps({"stress_workload": stress_leg()}), flush=True)
+        return
     shape = shape_of(3)
     R, H, W, T, dk, dv = shape.R, shape.H, shape.W, shape.T, shape.dk, shape.dv
     t_gen = time.perf_counter()
@@ -1047,6 +1184,10 @@ def main():
     par = [None] + [up(ep["parents"][t].astype(np.int32)) for t in range(1, T)]
     o = torch.empty((R * W, H, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.only == "multi_layer":
+        print(json.dumps({"multi_layer": multi_layer_leg(shape, max(args.layers, 1), q, k, v, al, be, par,
+                                                         up(ep["S0"]))}), flush=True)
+        return
     lay = Onela(R, H, dk, dv, W, T, stream=stream)
     if args.beams_per_block:
         lay.set_beams_per_block(args.beams_per_block)
