@@ -97,15 +97,25 @@ onela_status drain(onela_ctx* ctx) {
     return ONELA_OK;
 }
 
-int auto_beams_per_block(const onela_ctx* ctx, int n_pairs) {
+struct LaunchShape {
+    int beams_per_block;
+    bool half_chunks;   // the general body takes chunks of kChunk / 2 beams
+};
+
+LaunchShape auto_launch_shape(const onela_ctx* ctx, int n_pairs) {
     // Two workgroups fit on each of the 256 CUs: aim for at least 512 of
     // them, while keeping as many beams as possible per workgroup (its S0
-    // slice stays in registers across them).
+    // slice stays in registers across them). A launch that cannot reach 512
+    // workgroups with kChunk-beam chunks (few requests and heads) splits its
+    // beams at half that length instead, for twice the workgroups.
     const int W = ctx->cfg.beam_width;
+    const int want = (512 + n_pairs - 1) / n_pairs;
     const int chunks = (W + onela::kChunk - 1) / onela::kChunk;
-    int splits = std::max(1, std::min(chunks, (512 + n_pairs - 1) / n_pairs));
-    const int per = (chunks + splits - 1) / splits;
-    return per * onela::kChunk;
+    const bool half = chunks < want && W > onela::kChunk / 2;
+    const int len = half ? onela::kChunk / 2 : onela::kChunk;
+    const int n = (W + len - 1) / len;
+    const int splits = std::max(1, std::min(n, want));
+    return {((n + splits - 1) / splits) * len, half};
 }
 
 }  // namespace
@@ -387,7 +397,9 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
         p.o_bf16 = o16 ? o16 + rows * H * c.d_v : nullptr;
         p.delta_out = delta_out ? delta_out + rows * H * c.d_v : nullptr;
         p.n_req = n;
-        p.beams_per_block = ctx->beams_per_block ? ctx->beams_per_block : auto_beams_per_block(ctx, n * c.num_heads);
+        LaunchShape shape = auto_launch_shape(ctx, n * c.num_heads);
+        if (ctx->beams_per_block) shape = {ctx->beams_per_block, false};
+        p.beams_per_block = shape.beams_per_block;
         p.n_splits = (c.beam_width + p.beams_per_block - 1) / p.beams_per_block;
         for (int i = 0; i < n; ++i) {
             p.slot[i] = reqs[i0 + i];
@@ -400,7 +412,7 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
                          : n_first == n  ? onela::kStepFirst
                          : n_first == 0  ? onela::kStepHist
                                          : onela::kStepAny;
-        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, mode, p, ctx->stream);
+        hipError_t e = onela::launch_step(c.d_k, c.d_v, fused, mode, shape.half_chunks, p, ctx->stream);
         if (e != hipSuccess) return hip_fail(ctx, e, "step launch");
         if (!ctx->graph_mode)                     // (graph mode: the launch advances the device counters)
             for (int i = 0; i < n; ++i) ctx->steps[reqs[i0 + i]] += 1;

@@ -47,7 +47,7 @@ struct StepParams {
     float norm_eps;
     uint16_t* o_bf16;           // [n_req*W][H][DV] bf16
     int32_t write_index;        // 1: this launch writes the next step's ancestry rows and order
-    int32_t beams_per_block;    // multiple of kChunk, or >= W
+    int32_t beams_per_block;    // multiple of the chunk length, or >= W
     int32_t n_splits;           // ceil(W / beams_per_block)
     int32_t n_req;
     int32_t slot[kMaxReqPerLaunch];  // request id of call-local request i
@@ -128,7 +128,9 @@ hipError_t launch_init_s0(int dk, int dv, const float* S0, uint16_t* planes, int
 // ancestral record to gather), none at its first step, or either (graph mode,
 // where the step index is on the device, or requests at mixed depths).
 constexpr int kStepFirst = 0, kStepHist = 1, kStepAny = 2;
-hipError_t launch_step(int dk, int dv, bool fused, int mode, const StepParams& p, hipStream_t s);
+// half_chunks: the general body takes kChunk / 2 beams per chunk (small
+// launches; beams_per_block a multiple of kChunk / 2), else kChunk.
+hipError_t launch_step(int dk, int dv, bool fused, int mode, bool half_chunks, const StepParams& p, hipStream_t s);
 // Set the launch attributes the step kernel needs for this shape (once, before any launch).
 hipError_t prepare_step(int dk, int dv, int T_max, int W);
 // steps[req] = steps_value, epoch[req] = epoch_value (a request restarts).

@@ -130,9 +130,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // records), so no record is gathered. With nothing to gather, its chunks are
 // half as long: shorter staging and compute phases interleave better between
 // the workgroups that share a CU.
-template <int DK, int DV, bool FUSED, bool HIST>
+// HCH: beams per chunk of the general body, kChunk, or kChunk / 2 for
+// launches too small to fill the GPU (more workgroups, each with fewer beams).
+template <int DK, int DV, bool FUSED, bool HIST, int HCH>
 __device__ __forceinline__ void step_body(const StepParams& p) {
-    constexpr int CH = HIST ? kChunk : kChunk / 2;
+    constexpr int CH = HIST ? HCH : kChunk / 2;
     constexpr int NW = DV / kRowsPerWave;
     constexpr int NT = 64 * NW;
     constexpr int KS = DK / 32;        // MFMA k-steps
@@ -161,7 +163,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] processing order (W <= kOrderMax)
     int* pos_s = reinterpret_cast<int*>(xs);                        // [Wp] before the beam loop: step t-1 positions
     int* ck_s = pos_s + Wp;                                         // [Wp] before the beam loop: sort keys
-    static_assert(!HIST || 2 * CH * XS * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q staging area");
+    static_assert(!HIST || (2 * CH * XS + CH * VS) * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q/v staging area");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -655,15 +657,15 @@ __device__ __forceinline__ int step_request(const StepParams& p) {
 // gathers when its request is at its first step, which the host cannot know
 // in graph mode (the step index lives on the device). The two bodies in one
 // kernel raise its register pressure, so uniform launches keep their own.
-template <int DK, int DV, bool FUSED, int MODE>
+template <int DK, int DV, bool FUSED, int MODE, int HCH>
 __global__ __launch_bounds__(step_threads<DV>()) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const StepParams p) {
     if constexpr (MODE == kStepAny) {
         const int ri = step_request(p);
         const int t = p.dev_steps ? p.dev_steps[p.slot[ri]] + 1 : p.t[ri];
-        if (t <= 1) step_body<DK, DV, FUSED, false>(p);
-        else step_body<DK, DV, FUSED, true>(p);
+        if (t <= 1) step_body<DK, DV, FUSED, false, HCH>(p);
+        else step_body<DK, DV, FUSED, true, HCH>(p);
     } else {
-        step_body<DK, DV, FUSED, MODE == kStepHist>(p);
+        step_body<DK, DV, FUSED, MODE == kStepHist, HCH>(p);
     }
 }
 
@@ -678,13 +680,18 @@ template <int DK, int DV>
 hipError_t prepare_step_t(int T_max, int W) {
     const size_t lds = step_lds_bytes(DK, DV, T_max, W);
     if (lds <= 65536) return hipSuccess;
+    constexpr int S = kChunk / 2;
     const void* kernels[] = {
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepFirst>),
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepHist>),
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepAny>),
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepFirst>),
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepHist>),
-        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepAny>)};
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepFirst, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepHist, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepAny, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepHist, S>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, false, kStepAny, S>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepFirst, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepHist, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepAny, kChunk>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepHist, S>),
+        reinterpret_cast<const void*>(&step_kernel<DK, DV, true, kStepAny, S>)};
     for (const void* k : kernels) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -692,19 +699,24 @@ hipError_t prepare_step_t(int T_max, int W) {
     return hipSuccess;
 }
 
-template <int DK, int DV, bool FUSED>
+template <int DK, int DV, bool FUSED, int HCH>
 void launch_step_mode(int mode, dim3 grid, dim3 block, size_t lds, const StepParams& p, hipStream_t s) {
-    if (mode == kStepFirst) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepFirst>), grid, block, lds, s, p);
-    else if (mode == kStepHist) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepHist>), grid, block, lds, s, p);
-    else hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepAny>), grid, block, lds, s, p);
+    if (mode == kStepFirst) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepFirst, kChunk>), grid, block, lds, s, p);
+    else if (mode == kStepHist) hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepHist, HCH>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((step_kernel<DK, DV, FUSED, kStepAny, HCH>), grid, block, lds, s, p);
 }
 
 template <int DK, int DV>
-hipError_t launch_step_t(bool fused, int mode, const StepParams& p, hipStream_t s) {
+hipError_t launch_step_t(bool fused, int mode, bool half_chunks, const StepParams& p, hipStream_t s) {
     const size_t lds = step_lds_bytes(DK, DV, p.T_max, p.W);
     const dim3 grid(p.n_req * p.H * p.n_splits), block(step_threads<DV>());
-    if (fused) launch_step_mode<DK, DV, true>(mode, grid, block, lds, p, s);
-    else launch_step_mode<DK, DV, false>(mode, grid, block, lds, p, s);
+    if (half_chunks) {
+        if (fused) launch_step_mode<DK, DV, true, kChunk / 2>(mode, grid, block, lds, p, s);
+        else launch_step_mode<DK, DV, false, kChunk / 2>(mode, grid, block, lds, p, s);
+    } else {
+        if (fused) launch_step_mode<DK, DV, true, kChunk>(mode, grid, block, lds, p, s);
+        else launch_step_mode<DK, DV, false, kChunk>(mode, grid, block, lds, p, s);
+    }
     return hipGetLastError();
 }
 
@@ -752,11 +764,13 @@ hipError_t launch_set_counters(int32_t* dev_steps, int32_t* dev_epoch, int req, 
     return hipGetLastError();
 }
 
-hipError_t launch_step(int dk, int dv, bool fused, int mode, const StepParams& p, hipStream_t s) {
+hipError_t launch_step(int dk, int dv, bool fused, int mode, bool half_chunks, const StepParams& p, hipStream_t s) {
     if (mode != kStepFirst && mode != kStepHist && mode != kStepAny) return hipErrorInvalidValue;
-    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, mode, p, s);
-    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, mode, p, s);
-    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, mode, p, s);
+    if (half_chunks && p.beams_per_block % (kChunk / 2) != 0) return hipErrorInvalidValue;
+    if (!half_chunks && p.beams_per_block % kChunk != 0 && p.beams_per_block < p.W) return hipErrorInvalidValue;
+    if (dk == 32 && dv == 32) return launch_step_t<32, 32>(fused, mode, half_chunks, p, s);
+    if (dk == 64 && dv == 64) return launch_step_t<64, 64>(fused, mode, half_chunks, p, s);
+    if (dk == 128 && dv == 128) return launch_step_t<128, 128>(fused, mode, half_chunks, p, s);
     return hipErrorInvalidValue;
 }
 
