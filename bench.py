@@ -52,6 +52,7 @@ COUNTER_KERNELS = [
     ("prefill_kernel<128, 128, true> (5120-token prompts)", "::prefill_kernel<128, 128, true>"),
     ("projection probe, operands streamed", "projection_kernel"),
     ("projection probe, operands L2-resident", "projection_kernel"),
+    ("projection probe, operands L2-resident, W = 1024", "projection_kernel"),
     ("MFMA loop probe", "mfma_loop_kernel"),
     ("copy probe", "::copy_kernel"),
 ]
@@ -71,7 +72,8 @@ def counters_from(dirs, command: str) -> str:
     over SQ_WAVES. A step kernel row takes both instantiations (the first step's,
     which gathers no records, and the general one). The projection probe's
     dispatches are split in launch order:
-    the bench runs the streamed form first, then the L2-resident one.
+    the bench runs the streamed form first, then the L2-resident one, then
+    the L2-resident one with W = 1024.
     """
     import csv
     import glob
@@ -88,9 +90,10 @@ def counters_from(dirs, command: str) -> str:
                     agent = {k: int(r[k]) for k in ("Simd_Count", "Cu_Count", "Num_Xcc")}
         for label, frag in COUNTER_KERNELS:
             disp = [c for (i, n), c in sorted(rows.items()) if frag in n]
-            if frag == "projection_kernel":
-                half = len(disp) // 2
-                disp = disp[:half] if "streamed" in label else disp[half:]
+            if frag == "projection_kernel":   # three equal runs, in this order
+                third = len(disp) // 3
+                part = 0 if "streamed" in label else 2 if "1024" in label else 1
+                disp = disp[part * third:(part + 1) * third]
             n_disp[label] = max(n_disp.get(label, 0), len(disp))
             for c in disp:
                 for name, v in c.items():
@@ -540,6 +543,16 @@ def probe_leg(shape, q, k, S0):
     flops = R * H * 2 * W * 2 * dv * dk
     tflops = flops / t_proj / 1e12
     res_tflops = flops / t_res / 1e12
+    # the same probe with four times the beams per pair (W = 1024, drawn unit-norm-scale operands,
+    # 8 resident pairs): how much of the W = 256 rate is the fixed cost of each pair (its 64 KB of S0
+    # fragments, the first chunk's staging) rather than the matrix cores
+    W4 = 4 * W
+    g = torch.Generator(device=q[0].device).manual_seed(5)
+    k4 = (torch.randn((R * W4, H, dk), generator=g, device=q[0].device) / dk ** 0.5).to(torch.bfloat16).view(torch.int16)
+    q4 = (torch.randn((R * W4, H, dk), generator=g, device=q[0].device) / dk ** 0.5).to(torch.bfloat16).view(torch.int16)
+    t_w4 = timed(lambda: probes.projection(pl, k4, q4, W4, colsum, resident_pairs=8), 20)
+    w4_tflops = 4 * flops / t_w4 / 1e12
+    del k4, q4
     operands = R * W * H * 2 * dk * 2 + R * H * dv * dk * 4          # k, q (bf16) and S0
     p_bytes = R * 2 * W * H * dv * 4                                  # P itself, were it written in float32
     cap = lambda nbytes: flops / (nbytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_PEAK_TFLOPS
@@ -556,6 +569,8 @@ def probe_leg(shape, q, k, S0):
              "achieved_tflops": res_tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": res_tflops / BF16_PEAK_TFLOPS,
              "issued_tflops": 2 * res_tflops, "issued_frac": 2 * res_tflops / BF16_PEAK_TFLOPS,
              "issued_frac_of_measured_mfma_loop": 2 * res_tflops / loop_tflops,
+             "w1024_resident": {"us_per_launch": t_w4 * 1e6, "achieved_tflops": w4_tflops,
+                                "frac": w4_tflops / BF16_PEAK_TFLOPS, "issued_frac": 2 * w4_tflops / BF16_PEAK_TFLOPS},
              "full_footprint": {"us_per_launch": t_proj * 1e6, "achieved_tflops": tflops,
                                 "frac": tflops / BF16_PEAK_TFLOPS, "issued_frac": 2 * tflops / BF16_PEAK_TFLOPS,
                                 "operand_gbs": operands / t_proj / 1e9},
@@ -1293,6 +1308,7 @@ def main():
             "method": "projection-only probe with the step kernel's tiles and S0 planes, operands of 8 pairs "
                       "resident in L2",
             "streamed_frac": mp["full_footprint"]["frac"],
+            "w1024_resident_frac": mp["w1024_resident"]["frac"],
             "in_fused_step_frac": proj_tflops / BF16_PEAK_TFLOPS,
             "hbm_cap_frac": mp["hbm_cap_frac"],
             "target_frac": 0.4,
