@@ -333,14 +333,15 @@ def _counter_rows(d):
     return rows
 
 
-def profile_by_depth(leg: str, fetch_dir: str, write_dir: str, counter_dirs, copy_mib: int, command: str) -> str:
+def profile_by_depth(leg: str, fetch_dir: str, write_dir: str, counter_dirs, copy_mib: int, command: str,
+                     out_dir: str = "") -> str:
     """Per-depth HBM traffic and counters of step_kernel in a run of one bench
     leg alone (`bench.py --only stress` or `--only multi_layer` under
     rocprofv3 --pmc): FETCH_SIZE and WRITE_SIZE scaled by the same counters on
     a plain copy of copy_mib MiB in the same run, set against the algorithmic
     bytes of each depth from the realised parents; the other counter runs give
     wave waiting, L1-to-L2 read requests and MFMA / LDS activity per depth.
-    Writes profiles/<kernel>_<workload>_by_depth.txt and returns its text."""
+    Writes <out_dir or profiles/>/<kernel>_<workload>_by_depth.txt and returns its text."""
     if leg == "stress":
         from workload.gen_device import all_parents
 
@@ -350,8 +351,10 @@ def profile_by_depth(leg: str, fetch_dir: str, write_dir: str, counter_dirs, cop
         fname = "step_kernel_r64_h32_w1024_t7_zipf_by_depth.txt"
         what = "stress workload r64_h32_d128_w1024_t7, Zipf(1.2) parents"
     elif leg == "multi_layer":
+        from workload.gen import parents_for
+
         shape = shape_of(3)
-        parents = make_episode(shape, with_s0=False)["parents"]
+        parents = np.stack([parents_for(shape, r) for r in range(shape.R)], axis=1)
         per_step = 4
         fname = "step_kernel_4layers_r32_h16_w256_t5_by_depth.txt"
         what = ("4 GDN layers of r32_h16_d128_w256_t5 sharing one ancestry index, eager and graph-replayed "
@@ -438,7 +441,7 @@ def profile_by_depth(leg: str, fetch_dir: str, write_dir: str, counter_dirs, cop
         *lines,
         "",
     ])
-    path = os.path.join(ROOT, "profiles", fname)
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), fname)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     open(path, "w").write(text)
     return text

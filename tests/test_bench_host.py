@@ -91,3 +91,51 @@ def test_counter_summary_arithmetic(tmp_path, monkeypatch):
     assert cells[5] == "20.0%"                        # bank conflicts 2e4 / 1e5
     assert cells[6] == "60%" and cells[7] == "10%"    # wait / issue over wave cycles
     assert cells[8] == "2100"                         # VALU per wave (2.1e5 / 100)
+
+
+def test_profile_by_depth_arithmetic(tmp_path):
+    """Per-depth traffic summary of the 4-layer leg from synthetic FETCH_SIZE /
+    WRITE_SIZE runs: every layer-step of depth t reports (100 + t) MB fetched
+    and 50 MB written as counted, a 64 MiB copy counts half its bytes as fetched
+    and all as written, so the scaled bytes are 2 (100 + t) MB and 50 MB."""
+    agent = {"Simd_Count": 1024, "Cu_Count": 256, "Num_Xcc": 8}
+    name = "void onela::(anonymous namespace)::step_kernel<128, 128, false, 1, 64>(onela::StepParams)"
+    T, layers, episodes = 5, 4, 2
+    copy = 64 * 2.0 ** 20
+    runs = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = [(0, "__amd_rocclr_copyBuffer", {counter: (copy / 2 if counter == "FETCH_SIZE" else copy) / 1024})]
+        i = 1
+        for _ in range(episodes):
+            for t in range(T):
+                for _ in range(layers):
+                    mb = (100 + t + 1) * 1e6 if counter == "FETCH_SIZE" else 50e6
+                    rows.append((i, name, {counter: mb / 1024}))
+                    i += 1
+        d = str(tmp_path / counter)
+        _write_counter_run(d, rows, agent)
+        runs[counter] = d
+    text = bench.profile_by_depth("multi_layer", runs["FETCH_SIZE"], runs["WRITE_SIZE"], [], 64, "test",
+                                  out_dir=str(tmp_path))
+    assert os.path.exists(tmp_path / "step_kernel_4layers_r32_h16_w256_t5_by_depth.txt")
+    lines = [line for line in text.splitlines() if line.startswith("| ") and line[2].isdigit()]
+    assert len(lines) == T
+    shape = shape_of(3)
+    par = np.stack([parents_for(shape, r) for r in range(shape.R)], axis=1)
+    for t, line in enumerate(lines):
+        cells = [c.strip() for c in line.strip("|").split("|")]
+        assert int(cells[0]) == t + 1 and int(cells[1]) == episodes * layers
+        assert float(cells[2]) == pytest.approx(2 * (100 + t + 1), abs=0.05)      # fetch MB, scaled
+        assert float(cells[3]) == pytest.approx(50.0, abs=0.05)                   # write MB
+        alg = bench.step_bytes(shape, par, t + 1)["total"]
+        assert float(cells[5]) == pytest.approx(alg / 1e6, abs=0.05)
+        assert float(cells[6]) == pytest.approx((2 * (100 + t + 1) + 50) * 1e6 / alg, abs=5e-4)
+
+
+def test_depth_stats_percentiles():
+    per = np.array([[float(i), 10.0 * i] for i in range(1, 11)])   # 10 episodes, 2 depths
+    st = bench.depth_stats(per)
+    assert st["episodes"] == 10
+    assert st["median"] == [5.5, 55.0]
+    assert st["p10"] == [round(float(np.percentile(per[:, 0], 10)), 2), round(float(np.percentile(per[:, 1], 10)), 2)]
+    assert st["p90"][1] == round(float(np.percentile(per[:, 1], 90)), 2)
