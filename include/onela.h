@@ -249,6 +249,16 @@ onela_status onela_set_graph_mode(onela_ctx* ctx, int32_t on);
  * 64. Results do not depend on it; only the launch shape does. */
 onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
 
+/* Beam processing order of the step kernel: -1 = automatic (default), 0 =
+ * beam-index order, 1 = ancestry order (siblings adjacent, so that one chunk
+ * of beams gathers mostly the same ancestral records; beam widths up to 1024).
+ * Automatic orders a launch when its (request, head) pairs hold at least 32768
+ * beams in all: below that a launch is bound by each workgroup's dependent
+ * loads, which the ordering lengthens. Results do not depend on it (every
+ * beam's arithmetic is its own); only the records each chunk shares do.
+ * Returns ONELA_E_INVALID_ARG for any other value. */
+onela_status onela_set_beam_order(onela_ctx* ctx, int32_t mode);
+
 /* ---- inspection (synchronous; for tests and accounting) ---------------- */
 
 /* Steps done by `req` in the current episode (0 after init or reset). */

@@ -29,6 +29,7 @@ struct onela_ctx {
     std::vector<int32_t> epoch;      // episode number per request; a device error word counts only
                                      // if it carries the current one, so reset needs no device work
     int32_t beams_per_block = 0;     // 0 = automatic
+    int32_t beam_order = -1;         // -1 = automatic, 0 = beam-index order, 1 = ancestry order
     std::string last_error;
     uint64_t s0_bytes = 0, rec_bytes = 0, idx_bytes = 0;
     // Layers of one model share one ancestry index: the owner allocates and
@@ -100,7 +101,12 @@ onela_status drain(onela_ctx* ctx) {
 struct LaunchShape {
     int beams_per_block;
     bool half_chunks;   // the general body takes chunks of kChunk / 2 beams
+    bool order_beams;   // beams processed in ancestry order
 };
+
+bool order_beams(const onela_ctx* ctx, int n_pairs) {
+    return (long)n_pairs * ctx->cfg.beam_width >= onela::kOrderMinBeams;
+}
 
 LaunchShape auto_launch_shape(const onela_ctx* ctx, int n_pairs) {
     // Two workgroups fit on each of the 256 CUs: aim for at least 512 of
@@ -115,7 +121,7 @@ LaunchShape auto_launch_shape(const onela_ctx* ctx, int n_pairs) {
     const int len = half ? onela::kChunk / 2 : onela::kChunk;
     const int n = (W + len - 1) / len;
     const int splits = std::max(1, std::min(n, want));
-    return {((n + splits - 1) / splits) * len, half};
+    return {((n + splits - 1) / splits) * len, half, order_beams(ctx, n_pairs)};
 }
 
 }  // namespace
@@ -321,6 +327,12 @@ onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams) {
     return ONELA_OK;
 }
 
+onela_status onela_set_beam_order(onela_ctx* ctx, int32_t mode) {
+    if (!ctx || mode < -1 || mode > 1) return ONELA_E_INVALID_ARG;
+    ctx->beam_order = mode;
+    return ONELA_OK;
+}
+
 // One decode step for the listed requests. fused: q, k, alpha, beta are raw
 // projections (gates non-null) and o goes to o16 as bf16; else o is float32.
 static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs, const uint16_t* q,
@@ -398,8 +410,10 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
         p.delta_out = delta_out ? delta_out + rows * H * c.d_v : nullptr;
         p.n_req = n;
         LaunchShape shape = auto_launch_shape(ctx, n * c.num_heads);
-        if (ctx->beams_per_block) shape = {ctx->beams_per_block, false};
+        if (ctx->beams_per_block) shape = {ctx->beams_per_block, false, shape.order_beams};
+        if (ctx->beam_order >= 0) shape.order_beams = ctx->beam_order == 1;
         p.beams_per_block = shape.beams_per_block;
+        p.order_beams = shape.order_beams ? 1 : 0;
         p.n_splits = (c.beam_width + p.beams_per_block - 1) / p.beams_per_block;
         for (int i = 0; i < n; ++i) {
             p.slot[i] = reqs[i0 + i];

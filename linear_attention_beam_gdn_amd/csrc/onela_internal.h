@@ -14,6 +14,11 @@ constexpr int kMaxReqPerLaunch = 64;
 constexpr int kChunk = 64;
 // Widest beam set that is processed in ancestry order (the order lives in LDS).
 constexpr int kOrderMax = 1024;
+// Launches with fewer (request, head) beam sets than this many beams in all
+// keep the natural beam order: they are bound by the latency of each
+// workgroup's dependent loads, which the ordering lengthens by one round, not
+// by the record traffic it saves.
+constexpr long kOrderMinBeams = 32768;
 
 struct StepParams {
     // caller inputs / outputs
@@ -47,6 +52,7 @@ struct StepParams {
     float norm_eps;
     uint16_t* o_bf16;           // [n_req*W][H][DV] bf16
     int32_t write_index;        // 1: this launch writes the next step's ancestry rows and order
+    int32_t order_beams;        // 1: beams are processed in ancestry order (W <= kOrderMax only)
     int32_t beams_per_block;    // multiple of the chunk length, or >= W
     int32_t n_splits;           // ceil(W / beams_per_block)
     int32_t n_req;

@@ -256,7 +256,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     int* anc_next = p.anc + ((size_t)(t & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* ord_next = p.order + ((size_t)(t & 1) * p.max_requests + slot) * W;
 
-    const bool ordered = W <= kOrderMax;
+    const bool ordered = p.order_beams && W <= kOrderMax;
     __builtin_amdgcn_sched_barrier(0);
 
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
@@ -278,7 +278,10 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     // beam's arithmetic is independent of it. Every workgroup of a request
     // derives the same order (a deterministic rank), and one workgroup of the
     // index owner writes it for the next step. Wider beam sets than
-    // kOrderMax keep the natural order.
+    // kOrderMax, and launches the host leaves unordered, keep the natural
+    // order (and write it, so that a later ordered step reads a permutation).
+    if (!ordered && W <= kOrderMax && p.write_index && h == 0 && split == 0)
+        for (int i = tid; i < W; i += NT) ord_next[i] = i;
     if (ordered) {
         if (depth == 0) {
             for (int i = tid; i < W; i += NT) ord_s[i] = i;

@@ -34,7 +34,7 @@ EXPORTED = (
     "onela_rs_create", "onela_rs_destroy", "onela_rs_init_request", "onela_rs_step", "onela_rs_reset",
     "onela_rs_sync", "onela_rs_get_memory",
     "onela_init_requests_from_prompts", "onela_prefill", "onela_create_sharing_index", "onela_set_graph_mode",
-    "onela_step_raw",
+    "onela_step_raw", "onela_set_beam_order",
 )
 
 
@@ -74,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "onela_reset": (i32, [vp, i32]),
         "onela_sync": (i32, [vp]),
         "onela_set_beams_per_block": (i32, [vp, i32]),
+        "onela_set_beam_order": (i32, [vp, i32]),
         "onela_get_step": (i32, [vp, i32, p_i32]),
         "onela_get_ancestry": (i32, [vp, i32, vp]),
         "onela_get_records": (i32, [vp, i32, i32, i32, vp, vp, vp]),
@@ -252,6 +253,10 @@ class Onela:
 
     def set_beams_per_block(self, beams: int):
         self._check(self.lib.onela_set_beams_per_block(self._ctx, beams), "onela_set_beams_per_block")
+
+    def set_beam_order(self, mode: int):
+        """-1 automatic, 0 beam-index order, 1 ancestry order (onela_set_beam_order)."""
+        self._check(self.lib.onela_set_beam_order(self._ctx, mode), "onela_set_beam_order")
 
     def get_step(self, req: int) -> int:
         t = ctypes.c_int32()

@@ -36,10 +36,12 @@ def to_dev(a, dtype=None):
     return t.to(dev())
 
 
-def run_episode(shape, ep, S0, beams_per_block=0, keep_delta=True, reqs=None):
+def run_episode(shape, ep, S0, beams_per_block=0, keep_delta=True, reqs=None, beam_order=-1):
     """Run all T steps of the episode on the GPU. Returns per-step host arrays.
 
     o[t], delta[t]: [n*W][H][dv] float32; anc[t]: [n][W][max_steps] int32.
+    beam_order: -1 automatic, 0 index order, 1 ancestry order, or a list with
+    one of these per step.
     """
     n = len(ep["reqs"])
     reqs = list(range(n)) if reqs is None else reqs
@@ -47,6 +49,7 @@ def run_episode(shape, ep, S0, beams_per_block=0, keep_delta=True, reqs=None):
                 beam_width=shape.W, max_steps=shape.T)
     if beams_per_block:
         lay.set_beams_per_block(beams_per_block)
+    orders = beam_order if isinstance(beam_order, (list, tuple)) else [beam_order] * shape.T
     for i, r in enumerate(reqs):
         lay.init_request(r, to_dev(S0[i]))
     outs = {"o": [], "delta": [], "anc": []}
@@ -59,6 +62,7 @@ def run_episode(shape, ep, S0, beams_per_block=0, keep_delta=True, reqs=None):
         if d is not None:
             d.fill_(float("nan"))
         par = to_dev(ep["parents"][t].astype(np.int32)) if t > 0 else None
+        lay.set_beam_order(orders[t])
         lay.step(reqs, to_dev(ep["q"][t]), to_dev(ep["k"][t]), to_dev(ep["v"][t]),
                  to_dev(ep["alpha"][t]), to_dev(ep["beta"][t]), par, o, d)
         lay.sync()

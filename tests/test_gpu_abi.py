@@ -79,6 +79,11 @@ def test_host_misuse_is_rejected_without_side_effects():
     arr3 = (ctypes.c_int32 * 3)(0, 1, 0)
     assert lib.onela_step(lay._ctx, 3, arr3, p(q), p(k), p(v), p(a), p(b), None, p(o), None) == -1
     assert lay.get_step(0) == 0                    # nothing above advanced the request
+    # tuning knobs: values outside their ranges
+    assert lib.onela_set_beam_order(lay._ctx, 2) == -1
+    assert lib.onela_set_beam_order(lay._ctx, -2) == -1
+    assert lib.onela_set_beam_order(None, 0) == -1
+    assert lib.onela_set_beams_per_block(lay._ctx, 100) == -1
     # step 1 works, step 2 needs parents
     lay.step([0], q, k, v, a, b, None, o)
     q, k, v, a, b = _inputs(shape, ep, 1)

@@ -37,12 +37,13 @@ def _check_pairs(shape, ep, S0, outs, pairs, tol=None):
     return worst
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
-def test_parity_small_configs(cfg):
+@pytest.mark.parametrize("cfg,order", [(0, -1), (1, -1), (2, -1), (1, 1), (2, 1)])
+def test_parity_small_configs(cfg, order):
+    """Automatic beam order (index order at these sizes) and ancestry order forced."""
     shape = shape_of(cfg)
     ep, S0 = gh.episode(shape)
-    print(f"[parity] cfg={cfg} {shape.name}", flush=True)
-    outs = gh.run_episode(shape, ep, S0)
+    print(f"[parity] cfg={cfg} {shape.name} beam_order={order}", flush=True)
+    outs = gh.run_episode(shape, ep, S0, beam_order=order)
     pairs = [(i, h) for i in range(shape.R) for h in range(shape.H)]
     _check_pairs(shape, ep, S0, outs, pairs)
     outs["layer"].close()
@@ -74,15 +75,17 @@ def test_parity_ragged_beams(W, T, H, d):
     outs["layer"].close()
 
 
-@pytest.mark.parametrize("W,T,H,d", [(40, 12, 2, 64), (16, 20, 1, 128), (8, 64, 1, 32)])
-def test_parity_deep_histories(W, T, H, d):
+@pytest.mark.parametrize("W,T,H,d,order", [(40, 12, 2, 64, -1), (16, 20, 1, 128, -1), (8, 64, 1, 32, -1),
+                                           (40, 12, 2, 64, 1), (8, 64, 1, 32, 1)])
+def test_parity_deep_histories(W, T, H, d, order):
     """Histories longer than the short decode horizons of the pages' workload,
     up to the 64-step maximum: many older blocks of delta gathers per beam,
-    long ancestry rows, and (at 64 steps) the largest LDS footprint."""
+    long ancestry rows, and (at 64 steps) the largest LDS footprint; in the
+    automatic beam order and in ancestry order."""
     shape = shape_of(0, name=f"deep_t{T}", H=H, dk=d, dv=d, W=W, T=T, R=2)
     ep, S0 = gh.episode(shape)
-    print(f"[parity] deep history W={W} T={T} H={H} d={d}", flush=True)
-    outs = gh.run_episode(shape, ep, S0)
+    print(f"[parity] deep history W={W} T={T} H={H} d={d} beam_order={order}", flush=True)
+    outs = gh.run_episode(shape, ep, S0, beam_order=order)
     _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(2) for h in range(H)])
     outs["layer"].close()
 
@@ -126,6 +129,29 @@ def test_tile_size_invariance_and_determinism():
         for t in range(shape.T):
             assert np.array_equal(runs[0]["o"][t], other["o"][t])
             assert np.array_equal(runs[0]["delta"][t], other["delta"][t])
+    for r in runs:
+        r["layer"].close()
+
+
+def test_beam_order_invariance():
+    """The processing order only decides which beams share a chunk: index
+    order, ancestry order, and the two alternating from step to step (each
+    step then reads the order the previous one wrote, a permutation either
+    way) give bit-identical outputs, ancestry and records, equal to the
+    oracle's within the tolerance."""
+    shape = shape_of(1, R=2, T=5)
+    ep, S0 = gh.episode(shape)
+    modes = [0, 1, [1, 0, 1, 0, 1], [0, 1, 0, 1, 0], [1, 1, 0, 0, 1]]
+    runs = []
+    for m in modes:
+        print(f"[parity] beam order {m}", flush=True)
+        runs.append(gh.run_episode(shape, ep, S0, beam_order=m))
+    for other in runs[1:]:
+        for t in range(shape.T):
+            assert np.array_equal(runs[0]["o"][t], other["o"][t])
+            assert np.array_equal(runs[0]["delta"][t], other["delta"][t])
+            assert np.array_equal(runs[0]["anc"][t], other["anc"][t])
+    _check_pairs(shape, ep, S0, runs[2], [(i, h) for i in range(2) for h in range(0, shape.H, 5)])
     for r in runs:
         r["layer"].close()
 
