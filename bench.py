@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -753,8 +754,9 @@ SWEEP_FS_MAX_BYTES = 40 << 30       # full-state stores above this are skipped
 def sweep_leg(episodes=2):
     """OneLA against the full-state and replay comparators over a grid of
     operator shapes (W x d x T x (requests, heads)), on seeded inputs drawn on
-    the GPU. Per shape: mean launch time of each path over `episodes`
-    episodes (one event pair), speedups, and the persistent-state reduction
+    the GPU. Per shape: mean launch time of each path over at least
+    `episodes` episodes, and enough for a ~3 ms window (one event pair),
+    after one untimed and one sizing episode; speedups, and the persistent-state reduction
     against W full states per request and head. Returns the per-shape rows
     and the medians over the shapes."""
     import torch
@@ -791,13 +793,21 @@ def sweep_leg(episodes=2):
                         episode()
                         torch.cuda.synchronize()
                         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        # one timed episode sizes the run: at least `episodes`, and enough
+                        # for a window of ~3 ms, so that microsecond launches are not timed
+                        # over a handful of events
                         e0.record(stream)
-                        for _ in range(episodes):
+                        episode()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        n_ep = int(min(50, max(episodes, math.ceil(3.0 / max(e0.elapsed_time(e1), 1e-3)))))
+                        e0.record(stream)
+                        for _ in range(n_ep):
                             episode()
                         e1.record(stream)
                         torch.cuda.synchronize()
                         ctx.sync()
-                        return e0.elapsed_time(e1) * 1e-3 / (episodes * T)
+                        return e0.elapsed_time(e1) * 1e-3 / (n_ep * T)
 
                     ol = Onela(R, H, d, d, W, T, stream=stream)
                     t_ol = run(ol)

@@ -253,8 +253,10 @@ onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
  * beam-index order, 1 = ancestry order (siblings adjacent, so that one chunk
  * of beams gathers mostly the same ancestral records; beam widths up to 1024).
  * Automatic orders a launch when its (request, head) pairs hold at least 32768
- * beams in all: below that a launch is bound by each workgroup's dependent
- * loads, which the ordering lengthens. Results do not depend on it (every
+ * beams in all (below that a launch is bound by each workgroup's dependent
+ * loads, which the ordering lengthens) and each beam set is split over at most
+ * two workgroups (each workgroup ranks the whole set to process its share).
+ * Results do not depend on it (every
  * beam's arithmetic is its own); only the records each chunk shares do.
  * Returns ONELA_E_INVALID_ARG for any other value. */
 onela_status onela_set_beam_order(onela_ctx* ctx, int32_t mode);

@@ -104,8 +104,10 @@ struct LaunchShape {
     bool order_beams;   // beams processed in ancestry order
 };
 
-bool order_beams(const onela_ctx* ctx, int n_pairs) {
-    return (long)n_pairs * ctx->cfg.beam_width >= onela::kOrderMinBeams;
+bool order_beams(const onela_ctx* ctx, int n_pairs, int beams_per_block) {
+    const int W = ctx->cfg.beam_width;
+    const int splits = (W + beams_per_block - 1) / beams_per_block;
+    return (long)n_pairs * W >= onela::kOrderMinBeams && splits <= onela::kOrderMaxSplits;
 }
 
 LaunchShape auto_launch_shape(const onela_ctx* ctx, int n_pairs) {
@@ -121,7 +123,8 @@ LaunchShape auto_launch_shape(const onela_ctx* ctx, int n_pairs) {
     const int len = half ? onela::kChunk / 2 : onela::kChunk;
     const int n = (W + len - 1) / len;
     const int splits = std::max(1, std::min(n, want));
-    return {((n + splits - 1) / splits) * len, half, order_beams(ctx, n_pairs)};
+    const int bpb = ((n + splits - 1) / splits) * len;
+    return {bpb, half, order_beams(ctx, n_pairs, bpb)};
 }
 
 }  // namespace
@@ -410,7 +413,8 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
         p.delta_out = delta_out ? delta_out + rows * H * c.d_v : nullptr;
         p.n_req = n;
         LaunchShape shape = auto_launch_shape(ctx, n * c.num_heads);
-        if (ctx->beams_per_block) shape = {ctx->beams_per_block, false, shape.order_beams};
+        if (ctx->beams_per_block)
+            shape = {ctx->beams_per_block, false, order_beams(ctx, n * c.num_heads, ctx->beams_per_block)};
         if (ctx->beam_order >= 0) shape.order_beams = ctx->beam_order == 1;
         p.beams_per_block = shape.beams_per_block;
         p.order_beams = shape.order_beams ? 1 : 0;

@@ -17,8 +17,11 @@ constexpr int kOrderMax = 1024;
 // Launches with fewer (request, head) beam sets than this many beams in all
 // keep the natural beam order: they are bound by the latency of each
 // workgroup's dependent loads, which the ordering lengthens by one round, not
-// by the record traffic it saves.
+// by the record traffic it saves. So do launches that split a beam set over
+// more than kOrderMaxSplits workgroups: each workgroup ranks all W beams (W^2
+// comparisons) to process only its share of them.
 constexpr long kOrderMinBeams = 32768;
+constexpr int kOrderMaxSplits = 2;
 
 struct StepParams {
     // caller inputs / outputs
