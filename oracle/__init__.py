@@ -14,7 +14,8 @@ and pure-decay closed forms along parent paths, the delta-rule product form,
 the write-back property, exact associative recall with orthonormal keys,
 affinity in S0, beam-relabelling equivariance, replay == full state, a
 brute-force ancestry walk, and closed forms of the input-side gates and
-normalisation (`fused_inputs`). No function here is "parity unpinned".
+normalisation (`fused_inputs`, `unit_rows`). No function here is "parity
+unpinned".
 """
 from .gdn import (  # noqa: F401
     ancestry_walk,
@@ -22,4 +23,5 @@ from .gdn import (  # noqa: F401
     fused_inputs,
     prompt_state,
     replay_episode,
+    unit_rows,
 )

@@ -195,6 +195,14 @@ def _bf16_round(x32) -> np.ndarray:
     return (u.astype(np.uint32) << 16).view(np.float32)
 
 
+def unit_rows(x, eps=1e-6) -> np.ndarray:
+    """x / sqrt(sum of squares + eps) over the last axis, in float64: the
+    plain definition of the per-head L2 normalisation of q and k, before the
+    step rounds them to the bf16 it consumes."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
 def fused_inputs(q_raw, k_raw, a_raw, b_raw, A_log, dt_bias, eps=1e-6):
     """Decode-step inputs from raw projections.
 
@@ -202,7 +210,8 @@ def fused_inputs(q_raw, k_raw, a_raw, b_raw, A_log, dt_bias, eps=1e-6):
     A_log, dt_bias: [H]. Returns (q, k, alpha, beta): q and k divided by
     sqrt(sum of squares + eps) per head in float32 and rounded to bf16 (the
     precision the step consumes them in, so both sides take that rounding
-    decision in the same precision), alpha and beta in float64.
+    decision in the same precision; `unit_rows` is the float64 definition it
+    is pinned against), alpha and beta in float64.
     """
     def unit(x):
         x = np.asarray(x, dtype=np.float32)

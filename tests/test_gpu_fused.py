@@ -5,10 +5,12 @@ The oracle forms q, k, alpha, beta from the same raw projections
 * o (bf16): |o - o_ref| <= 1e-3 + 2^-8 |o_ref| (the step's 1e-3 plus the
   bf16 rounding of o, at most half a unit in the last place, 2^-9 relative);
 * delta (float32): 1e-3;
-* keys in the records: the oracle normalises in float32 and rounds to bf16 as
-  the kernel does, but the sums of squares are added in a different order, so
-  a key element may land on the neighbouring bf16 value: at most one unit in
-  the last place, in at most 1% of the elements;
+* keys in the records, against the float64 normalisation (`oracle.unit_rows`):
+  every element is one of the two bf16 values bracketing the exact value, and
+  the exact value's nearest one wherever that is farther from their midpoint
+  than the float32 error bound derived in tests/bf16_bounds.py (the kernel
+  normalises in float32 before rounding, as the oracle's `fused_inputs` does
+  with another summation order);
 * alpha in the records: 1e-5 relative (float32 exp/log1p against float64).
 """
 import numpy as np
@@ -22,7 +24,8 @@ EPS = 1e-6
 if torch.cuda.is_available():
     import gpu_harness as gh
     from linear_attention_beam_gdn_amd import Onela, OnelaError
-    from oracle import full_state_episode, fused_inputs
+    from bf16_bounds import check_rounded, fp32_unit_rel_bound
+    from oracle import full_state_episode, fused_inputs, unit_rows
     from workload import bf16_bits_to_f32, make_raw_episode, shape_of
 
 
@@ -73,9 +76,10 @@ def _check(shape, ep, outs, pairs):
             assert ed <= 1e-3, (i, h, t)
         a_rec, _, k_rec = outs["layer"].get_records(i, h, T * W)
         k_gpu = bf16_bits_to_f32(k_rec).reshape(T, W, -1)
-        diff = k_gpu != kn
-        assert diff.mean() <= 0.01, (i, h, diff.mean())
-        assert np.all(np.abs(k_gpu - kn) <= 2.0 ** -7 * np.abs(kn) + 1e-30), (i, h)
+        u = unit_rows(bf16_bits_to_f32(ep["k_raw"][:, i * W:(i + 1) * W, h]), eps=EPS)
+        bracket, exact, n_band, n_diff = check_rounded(k_gpu, u, fp32_unit_rel_bound(shape.dk))
+        gh.parity_log.record("key_elements_off_nearest", float(n_diff), float(n_band))
+        assert bracket and exact, (i, h, n_band, n_diff)
         np.testing.assert_allclose(a_rec.reshape(T, W), an, rtol=1e-5)
 
 

@@ -12,7 +12,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import ancestry_walk, full_state_episode, fused_inputs, prompt_state, replay_episode
+from oracle import ancestry_walk, full_state_episode, fused_inputs, prompt_state, replay_episode, unit_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -269,3 +269,42 @@ def test_fused_normalisation():
     norms = np.linalg.norm(base.astype(np.float64), axis=-1)
     assert np.all(np.abs(norms - 1.0) <= 2.0 ** -8)
     assert np.array_equal(base, k1)
+
+
+def test_unit_rows_definition():
+    """The float64 normalisation: (3, 4) -> (0.6, 0.8); unit length for
+    eps = 0; invariant under positive scaling (eps = 0); eps enters under the
+    square root: (3, 4) with eps = 11 has norm 5 / 6."""
+    x = np.array([[3.0, 4.0, 0.0]])
+    np.testing.assert_allclose(unit_rows(x, eps=0.0), [[0.6, 0.8, 0.0]], rtol=0, atol=1e-16)
+    np.testing.assert_allclose(unit_rows(x, eps=11.0), [[0.5, 2.0 / 3.0, 0.0]], rtol=1e-15)
+    rng = np.random.default_rng(8)
+    raw = rng.standard_normal((40, 3, 64))
+    u = unit_rows(raw, eps=0.0)
+    np.testing.assert_allclose(np.linalg.norm(u, axis=-1), 1.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(unit_rows(raw * 37.5, eps=0.0), u, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("d,eps", [(32, 1e-6), (64, 0.0), (128, 1e-6)])
+def test_fused_normalisation_against_float64(d, eps):
+    """fused_inputs takes the bf16 rounding of the normalised q and k in
+    float32 (the step's precision); against the float64 definition every
+    element is one of the two bf16 values that bracket the exact value, and
+    it is the exact value's nearest one wherever that is farther from their
+    midpoint than the derived float32 error bound (tests/bf16_bounds.py)."""
+    from bf16_bounds import check_rounded, fp32_unit_rel_bound
+    from workload import bf16_bits_to_f32
+
+    rng = np.random.default_rng(d)
+    bits = (rng.standard_normal((300, 4, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    raw = bf16_bits_to_f32(bits)                     # bf16-valued raw projections, as the step receives them
+    q, k, _, _ = fused_inputs(raw, raw, np.zeros((300, 4)), np.zeros((300, 4)), np.zeros(4), np.zeros(4), eps=eps)
+    u = unit_rows(raw, eps=eps)
+    for x in (q, k):
+        bracket, exact, n_band, n_diff = check_rounded(x, u, fp32_unit_rel_bound(d))
+        assert bracket and exact, (n_band, n_diff)
+        assert n_diff <= n_band
+    # a mistake in the definition shows: without eps under the root, or with the
+    # squares summed over the wrong axis, elements leave their bracket
+    bad = raw / np.sqrt(np.sum(raw * raw, axis=-2, keepdims=True))
+    assert not check_rounded(k, bad, fp32_unit_rel_bound(d))[0]
