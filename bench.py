@@ -204,6 +204,16 @@ def time_episodes(run, stream, episodes: int, T: int, instrumented: int = 10):
     return mean_launch_s, wall / episodes, np.median(per, axis=0), per
 
 
+def evict_caches(buf) -> None:
+    """Enqueue a read of `buf` (512 MiB or more): it replaces what the 256 MB
+    last-level cache and the L2s hold with clean lines of its own. (A write
+    would leave that much dirty data behind, whose write-backs the next kernel
+    would then pay for.)"""
+    import torch
+
+    torch.amax(buf.view(torch.int32))
+
+
 def depth_stats(per_us: np.ndarray) -> dict:
     """Median, p10 and p90 per depth (columns) of instrumented launch times in microseconds."""
     return {"median": [round(float(x), 2) for x in np.median(per_us, axis=0)],
@@ -851,7 +861,7 @@ def latency_leg(episodes=20, warmup=3, flush_mib=512):
     Per depth, median, p10 and p90 over `episodes` episodes with a HIP event
     pair around each launch, taken twice: warm (caches hold the previous
     episode's inputs and records) and cold (a `flush_mib` MiB buffer is
-    written, untimed, before every step, which evicts the 256 MB last-level
+    read, untimed, before every step, which evicts the 256 MB last-level
     cache and the L2s). Also the mean per launch of back-to-back warm episodes
     with no event between the launches (an event marker between two kernels
     costs the GPU a few microseconds, a visible share of launches this short),
@@ -863,7 +873,7 @@ def latency_leg(episodes=20, warmup=3, flush_mib=512):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    flush = torch.ones(flush_mib << 20, dtype=torch.uint8, device=dev)
     res = {}
     for cfg in (0, 1, 2):
         shape = shape_of(cfg)
@@ -889,7 +899,7 @@ def latency_leg(episodes=20, warmup=3, flush_mib=512):
                 lay.reset(r)
             for t in range(T):
                 if cold:
-                    flush.fill_(t + 1)                      # untimed: before the event pair
+                    evict_caches(flush)                     # untimed: before the event pair
                 if events is not None:
                     events[t][0].record(stream)
                 lay.step(reqs, *ins[t], par[t], o)
@@ -1252,6 +1262,27 @@ def main():
     mean_launch_s, wall_per_episode, med_t_us, per_t_us = time_episodes(episode, stream, args.steps, T,
                                                                         instrumented=20)
     lay.sync()
+    # Cold pass (outside the timed region): the 256 MB last-level cache evicted by an
+    # untimed 512 MiB read before every step, events around each launch. A layer that
+    # steps alone finds part of the previous steps' records in that cache; inside a model
+    # the other layers' steps evict them.
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    evict_caches(flush)
+    cold_per = []
+    for i in range(10):
+        for r in reqs:
+            lay.reset(r)
+        evc = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(T)]
+        for t in range(T):
+            evict_caches(flush)
+            evc[t][0].record(stream)
+            lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t], o)
+            evc[t][1].record(stream)
+        torch.cuda.synchronize()
+        cold_per.append([evc[t][0].elapsed_time(evc[t][1]) * 1e3 for t in range(T)])
+    del flush
+    lay.sync()
+    cold_per = np.array(cold_per)
 
     bytes_t = [step_bytes(shape, ep["parents"], t + 1) for t in range(T)]
     flops_t = [step_flops(shape, t + 1) for t in range(T)]
@@ -1289,6 +1320,14 @@ def main():
         "us_per_decode_step": ms_per_step * 1e3 / T,
         "us_by_depth_instrumented": [round(float(x), 2) for x in med_t_us],
         "us_by_depth_instrumented_stats": depth_stats(per_t_us),
+        "cold_cache": {
+            "what": ("the same launches with the 256 MB last-level cache evicted (an untimed 512 MiB read) "
+                     "before every step, events around each launch, 10 episodes; hbm_frac from the mean "
+                     "of the per-depth medians (event markers included, as in us_by_depth_instrumented)"),
+            "us_by_depth": depth_stats(cold_per),
+            "us_per_launch": float(np.mean(np.median(cold_per, axis=0))),
+            "hbm_frac": bytes_per_launch / (float(np.mean(np.median(cold_per, axis=0))) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        },
         "kernel_us_mean": mean_launch_s * 1e6,
         "unique_records_by_depth": [b["unique_records"] for b in bytes_t],
         "roofline": {
