@@ -207,3 +207,34 @@ def test_more_requests_than_one_launch():
     outs = gh.run_episode(shape, ep, S0, reqs=reqs)
     _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(70) for h in range(2)])
     outs["layer"].close()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_parity_random_shapes(seed):
+    """Seeded random shapes, parent patterns, gate extremes, launch shapes and
+    beam orders: every (request, head) pair against the oracle. Parents are
+    drawn uniformly, top-W of 4W or Zipf(1.2), or replaced by every beam
+    continuing beam 0 (one shared history) or beam b continuing beam b (W
+    independent chains)."""
+    rng = np.random.default_rng(4242 + seed)
+    d = int(rng.choice([32, 64, 128]))
+    W, T = int(rng.integers(1, 300)), int(rng.integers(1, 9))
+    R, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    pattern = str(rng.choice(["uniform", "topw4", "zipf"]))
+    shape = shape_of(0, name=f"random{seed}", R=R, H=H, dk=d, dv=d, W=W, T=T, parents=pattern)
+    ep, S0 = gh.episode(shape)
+    special = int(rng.integers(0, 4))
+    if special == 1:
+        ep["parents"][1:] = 0
+    elif special == 2:
+        ep["parents"][1:] = np.arange(W, dtype=ep["parents"].dtype)
+    elif special == 3:
+        for key in ("alpha", "beta"):
+            pick = rng.integers(0, 4, size=ep[key].shape)
+            ep[key] = np.where(pick == 0, 0.0, np.where(pick == 1, 1.0, ep[key])).astype(np.float32)
+    order, bpb = int(rng.choice([-1, 0, 1])), int(rng.choice([0, 64, 128]))
+    print(f"[parity] random seed={seed} R={R} H={H} d={d} W={W} T={T} parents={pattern} special={special} "
+          f"beam_order={order} beams_per_block={bpb}", flush=True)
+    outs = gh.run_episode(shape, ep, S0, beams_per_block=bpb, beam_order=order)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(R) for h in range(H)])
+    outs["layer"].close()
