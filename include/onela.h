@@ -246,19 +246,24 @@ onela_status onela_step_raw(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
 onela_status onela_set_graph_mode(onela_ctx* ctx, int32_t on);
 
 /* Beams handled by one workgroup (0 = automatic). Must be 0 or a multiple of
- * 64. Results do not depend on it; only the launch shape does. */
+ * 64, else ONELA_E_INVALID_ARG. Results do not depend on it; only the launch
+ * shape does: one workgroup projects the shared state once for all the beams
+ * it holds (OneLA abstract: the fused kernel reuses the shared state across
+ * beams), so fewer splits mean fewer reads of it. */
 onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
 
 /* Beam processing order of the step kernel: -1 = automatic (default), 0 =
  * beam-index order, 1 = ancestry order (siblings adjacent, so that one chunk
  * of beams gathers mostly the same ancestral records; beam widths up to 1024).
+ * Beams that share history share records (OneLA abstract: the ancestry index
+ * lists the transition records that make up each beam's history).
  * Automatic orders a launch when its (request, head) pairs hold at least 32768
  * beams in all (below that a launch is bound by each workgroup's dependent
  * loads, which the ordering lengthens) and each beam set is split over at most
  * two workgroups (each workgroup ranks the whole set to process its share).
- * Results do not depend on it (every
- * beam's arithmetic is its own); only the records each chunk shares do.
- * Returns ONELA_E_INVALID_ARG for any other value. */
+ * Results do not depend on it (every beam's arithmetic is its own); only the
+ * records each chunk shares do. Returns ONELA_E_INVALID_ARG for any other
+ * value. */
 onela_status onela_set_beam_order(onela_ctx* ctx, int32_t mode);
 
 /* ---- inspection (synchronous; for tests and accounting) ---------------- */
