@@ -121,8 +121,10 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
 onela_status onela_create_sharing_index(const onela_config* cfg, void* hip_stream, onela_ctx* index_owner,
                                         onela_ctx** out);
 
-/* Synchronise the stream and free everything the context owns. NULL is OK.
- * An index owner with live sharing contexts: ONELA_E_BAD_STATE. */
+/* Synchronise the stream and free everything the context owns (the shared
+ * states, record store and ancestry index of its requests; OneLA abstract:
+ * the state the method keeps per request). NULL is OK. An index owner with
+ * live sharing contexts: ONELA_E_BAD_STATE. */
 onela_status onela_destroy(onela_ctx* ctx);
 
 /* Load the shared prompt-derived state of request `req` and rewind it to
@@ -195,7 +197,9 @@ onela_status onela_step(onela_ctx* ctx, int32_t n_req, const int32_t* reqs,
 onela_status onela_reset(onela_ctx* ctx, int32_t req);
 
 /* Wait for the stream. Returns ONELA_E_PARENT_RANGE if any request is
- * poisoned by a bad parent index, ONELA_E_HIP on a HIP failure. */
+ * poisoned by a bad parent index (each beam continues a beam of the previous
+ * step; OneLA abstract: the ancestry index follows the beam tree), ONELA_E_HIP
+ * on a HIP failure. */
 onela_status onela_sync(onela_ctx* ctx);
 
 /* ---- input-side fusion ----------------------------------------------------
@@ -214,7 +218,9 @@ typedef struct {
     float norm_eps;         /* >= 0, added to the sum of squares (e.g. 1e-6) */
 } onela_gate_params;
 
-/* onela_step with raw inputs: q_raw, k_raw device bf16 [n_req*W][H][d_k]
+/* onela_step (the step of OneLA review, evolve.pub, "Summary", paper Eq. 2-4)
+ * with raw inputs, the fused input side above not being on the pages:
+ * q_raw, k_raw device bf16 [n_req*W][H][d_k]
  * (16-byte aligned), v as in onela_step, a_raw, b_raw device float32
  * [n_req*W][H], gates (host struct, device arrays), o_bf16 device bf16
  * [n_req*W][H][d_v] (8-byte aligned). delta_out (float32), parents, request
@@ -268,20 +274,26 @@ onela_status onela_set_beam_order(onela_ctx* ctx, int32_t mode);
 
 /* ---- inspection (synchronous; for tests and accounting) ---------------- */
 
-/* Steps done by `req` in the current episode (0 after init or reset). */
+/* Steps done by `req` in the current episode (0 after init or reset): the
+ * number of records each of its beams has appended (OneLA abstract:
+ * append-only transition records). */
 onela_status onela_get_step(onela_ctx* ctx, int32_t req, int32_t* t_done);
 
-/* Ancestry rows the last step of `req` used: host int32 [W][max_steps];
- * row b holds t_done-1 record ids (oldest first) and -1 after them. */
+/* Ancestry rows the last step of `req` used (OneLA abstract: the ancestry
+ * index lists the records that make up each beam's history): host int32
+ * [W][max_steps]; row b holds t_done-1 record ids (oldest first) and -1
+ * after them. */
 onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out);
 
-/* Records 0..n_rec-1 of (req, head), n_rec <= t_done*W. Host outputs, each
- * may be NULL: alpha float32 [n_rec], delta float32 [n_rec][d_v],
- * key bf16 bits [n_rec][d_k]. */
+/* Records 0..n_rec-1 of (req, head), n_rec <= t_done*W (OneLA review,
+ * evolve.pub, "Summary": a record holds (alpha_t, delta_t, k_t)). Host
+ * outputs, each may be NULL: alpha float32 [n_rec], delta float32
+ * [n_rec][d_v], key bf16 bits [n_rec][d_k]. */
 onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_t n_rec,
                                float* alpha, float* delta, uint16_t* key);
 
-/* Device bytes the context owns: S0 planes, record store, and in index_bytes
+/* Device bytes the context owns, the state whose size the method reduces
+ * (OneLA review, evolve.pub, "Summary"): S0 planes, record store, and in index_bytes
  * the ancestry index and beam order (none on a context sharing another's
  * index) plus five int32 words per request (error words, graph-mode
  * counters). */
@@ -350,10 +362,11 @@ onela_status onela_rs_sync(onela_rs_ctx* ctx);
 /* Device bytes of persistent state the comparator owns (S0, records, parents). */
 onela_status onela_rs_get_memory(const onela_rs_ctx* ctx, uint64_t* state_bytes);
 
-/* Static text for a status code. */
+/* Static text for a status code (a library utility: no passage defines it). */
 const char* onela_status_string(onela_status s);
 
-/* Text of the last HIP error seen by this context ("" if none). */
+/* Text of the last HIP error seen by this context ("" if none; a library
+ * utility: no passage defines it). */
 const char* onela_last_error(const onela_ctx* ctx);
 
 #ifdef __cplusplus
