@@ -1376,6 +1376,12 @@ def main():
     if args.layers > 0:
         S0_ml = S0_dev if S0_dev is not None else up(ep["S0"])
         out["multi_layer"] = multi_layer_leg(shape, args.layers, q, k, v, al, be, par, S0_ml)
+        # the same layers for the first request alone: launches of a few microseconds,
+        # where replaying a captured graph saves the per-launch host and dispatch work
+        cut = lambda xs: [x[:W] for x in xs]
+        out["multi_layer_one_request"] = multi_layer_leg(
+            shape_of(shape.cfg, R=1), args.layers, cut(q), cut(k), cut(v), cut(al), cut(be),
+            [None] + [x[:1] for x in par[1:]], S0_ml[:1])
     if not args.no_fullstate:
         out["fullstate_comparator"] = fullstate_leg(shape, q, k, v, al, be, par, o,
                                                     up(ep["S0"]) if S0_dev is None else S0_dev, stream,
