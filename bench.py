@@ -1164,7 +1164,7 @@ def main():
     ap.add_argument("--counters-from", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc runs of this bench into the counters file and exit")
     ap.add_argument("--counters-command", default="", help="commands recorded in the counters file")
-    ap.add_argument("--only", choices=("stress", "multi_layer"),
+    ap.add_argument("--only", choices=("stress", "multi_layer", "latency"),
                     help="run this leg alone (after the copy probe) and print its JSON, for per-depth profiles")
     ap.add_argument("--profile-by-depth", nargs="+", metavar="DIR",
                     help="with --only LEG: FETCH_DIR WRITE_DIR [COUNTER_DIR ...] of rocprofv3 --pmc runs of that leg "
@@ -1178,8 +1178,8 @@ def main():
                                     args.traffic_command))
         return
     if args.profile_by_depth:
-        if not args.only or len(args.profile_by_depth) < 2:
-            raise SystemExit("--profile-by-depth needs --only LEG and at least FETCH_DIR WRITE_DIR")
+        if args.only not in ("stress", "multi_layer") or len(args.profile_by_depth) < 2:
+            raise SystemExit("--profile-by-depth needs --only stress|multi_layer and at least FETCH_DIR WRITE_DIR")
         print(profile_by_depth(args.only, args.profile_by_depth[0], args.profile_by_depth[1],
                                args.profile_by_depth[2:], args.copy_probe or 256, args.counters_command))
         return
@@ -1201,6 +1201,9 @@ def main():
 
     if args.only == "stress":
         print(json.dumps({"stress_workload": stress_leg()}), flush=True)
+        return
+    if args.only == "latency":
+        print(json.dumps({"latency_configs": latency_leg()}), flush=True)
         return
     shape = shape_of(3)
     R, H, W, T, dk, dv = shape.R, shape.H, shape.W, shape.T, shape.dk, shape.dv
