@@ -1064,14 +1064,30 @@ def fullstate_leg(shape, q, k, v, al, be, par, o, S0, stream, onela_launch_s, on
 def _oracle_pair(args):
     import oracle
 
-    S0, q, k, v, a, b, par = args
+    S0, q, k, v, a, b, par, gpu = args
     t0 = time.perf_counter()
-    oracle.full_state_episode(S0, q, k, v, a, b, par)
-    return time.perf_counter() - t0
+    ref = oracle.full_state_episode(S0, q, k, v, a, b, par)
+    cpu_s = time.perf_counter() - t0
+    if gpu is None:
+        return cpu_s, None, None
+    g_o, g_d = gpu                                  # the GPU's o and delta of this pair, [T][W][dv]
+    return cpu_s, float(np.max(np.abs(g_o - ref["o"]))), float(np.max(np.abs(g_d - ref["delta"])))
 
 
-def cpu_baseline(shape, ep, n_pairs: int):
-    """Oracle (float64 full state per beam) on n_pairs (request, head) pairs, all steps."""
+def baseline_pairs(shape, n_pairs: int):
+    """The (request, head) pairs the CPU baseline runs (seeded)."""
+    rng = np.random.default_rng(7)
+    return [(int(rng.integers(shape.R)), int(rng.integers(shape.H))) for _ in range(n_pairs)]
+
+
+def cpu_baseline(shape, ep, n_pairs: int, S0=None, gpu_outputs=None, s0_label="the run's S0"):
+    """Oracle (float64 full state per beam) on n_pairs (request, head) pairs, all steps.
+
+    S0: the run's S0 per request [R][H][dv][dk] (host float32), or None for the
+    episode's drawn one. gpu_outputs: {(request, head): (o, delta)} of the GPU
+    path on the same inputs for some of the pairs; the oracle's results for
+    those are compared with them (max-abs), the same arithmetic the timing
+    runs anyway."""
     import multiprocessing as mp
 
     visible = len(os.sched_getaffinity(0))
@@ -1081,29 +1097,36 @@ def cpu_baseline(shape, ep, n_pairs: int):
     cores = max(1, min(visible, int(share)) if share.isdigit() and int(share) > 0 else visible)
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"                     # one BLAS thread per worker
-    rng = np.random.default_rng(7)
-    pairs = [(int(rng.integers(shape.R)), int(rng.integers(shape.H))) for _ in range(n_pairs)]
+    pairs = baseline_pairs(shape, n_pairs)
     W = shape.W
+    S0 = ep["S0"] if S0 is None else S0
+    gpu_outputs = gpu_outputs or {}
     jobs = []
     for (r, h) in pairs:
         sl = slice(r * W, (r + 1) * W)
         f = lambda key: bf16_bits_to_f32(ep[key][:, sl, h, :])
-        jobs.append((ep["S0"][r, h], f("q"), f("k"), f("v"), ep["alpha"][:, sl, h], ep["beta"][:, sl, h],
-                     ep["parents"][:, r, :]))
+        jobs.append((S0[r, h], f("q"), f("k"), f("v"), ep["alpha"][:, sl, h], ep["beta"][:, sl, h],
+                     ep["parents"][:, r, :], gpu_outputs.get((r, h))))
     ctx = mp.get_context("fork")
     with ctx.Pool(min(cores, n_pairs)) as pool:
         t0 = time.perf_counter()
         per_pair = pool.map(_oracle_pair, jobs)
         wall = time.perf_counter() - t0
     beam_steps = W * shape.T * n_pairs / shape.H       # a beam-step covers all H heads
+    checked = [x for x in per_pair if x[1] is not None]
     return {
         "value": beam_steps / wall,
         "unit": "beam-steps/s",
         "cores": min(cores, n_pairs),
         "kind": "oracle",
         "sample": (f"{n_pairs} (request, head) pairs of {shape.name}, all {shape.T} steps, float64 full state "
-                   f"per beam, from a drawn S0 (the oracle's cost does not depend on S0's values); "
-                   f"{wall:.1f} s wall, {sum(per_pair):.1f} s CPU; scaled by {shape.H} heads per beam-step"),
+                   f"per beam, from {s0_label}; {wall:.1f} s wall, {sum(x[0] for x in per_pair):.1f} s CPU; "
+                   f"scaled by {shape.H} heads per beam-step"),
+        "max_abs_err_vs_gpu": ({"o": max(x[1] for x in checked), "delta": max(x[2] for x in checked),
+                                "pairs": len({pr for pr in pairs if pr in gpu_outputs}), "bound": 1e-3,
+                                "what": "the GPU path's o and delta of one untimed episode of the same inputs "
+                                        "against the oracle's, over all steps and beams of these pairs"}
+                               if checked else None),
         "cpu_model": _cpu_model(),
         "host_cpus_visible": visible,
         "workers": min(cores, n_pairs),
@@ -1371,6 +1394,25 @@ def main():
         }
     if prefill_out is not None:
         out["prefill"] = prefill_out
+    # One untimed episode whose o and delta the CPU baseline checks for its first
+    # pairs (the same inputs and S0 as the timed episodes).
+    gpu_check, S0_host = {}, None
+    if not args.no_cpu_baseline and (S0_dev is not None or args.s0 != "prompt"):
+        S0_host = S0_dev.cpu().numpy() if S0_dev is not None else None
+        check = list(dict.fromkeys(baseline_pairs(shape, args.cpu_pairs)[:32]))   # (distinct pairs)
+        d_chk = torch.empty_like(o)
+        for r in reqs:
+            lay.reset(r)
+        got = {pr: ([], []) for pr in check}
+        for t in range(T):
+            lay.step(reqs, q[t], k[t], v[t], al[t], be[t], par[t], o, d_chk)
+            torch.cuda.synchronize()
+            for (r, h) in check:
+                got[(r, h)][0].append(o[r * W:(r + 1) * W, h].cpu().numpy())
+                got[(r, h)][1].append(d_chk[r * W:(r + 1) * W, h].cpu().numpy())
+        lay.sync()
+        gpu_check = {pr: (np.stack(a), np.stack(b)) for pr, (a, b) in got.items()}
+        del d_chk
     mem = lay.memory()
     lay.close()
     if not args.no_fused:
@@ -1400,7 +1442,10 @@ def main():
     if not args.no_sweep:
         out["operator_sweep"] = sweep_leg()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, ep, args.cpu_pairs)
+        out["cpu_baseline"] = cpu_baseline(
+            shape, ep, args.cpu_pairs, S0=S0_host, gpu_outputs=gpu_check,
+            s0_label=("the run's S0" if (S0_host is not None or args.s0 != "prompt") else
+                      "a drawn S0 (the oracle's cost does not depend on S0's values)"))
     print(json.dumps(out), flush=True)
 
 

@@ -139,3 +139,37 @@ def test_depth_stats_percentiles():
     assert st["median"] == [5.5, 55.0]
     assert st["p10"] == [round(float(np.percentile(per[:, 0], 10)), 2), round(float(np.percentile(per[:, 1], 10)), 2)]
     assert st["p90"][1] == round(float(np.percentile(per[:, 1], 90)), 2)
+
+
+def test_cpu_baseline_error_check(monkeypatch):
+    """The CPU baseline's check of the GPU outputs: outputs equal to the
+    oracle's give zero error; an output moved by a known amount in one element
+    gives exactly that error, on o or delta alone; pairs without outputs are
+    timed but not checked."""
+    from oracle import full_state_episode
+    from workload import bf16_bits_to_f32, make_episode
+
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    shape = shape_of(0, R=2, H=2, W=8, T=3)
+    ep = make_episode(shape)
+    pairs = bench.baseline_pairs(shape, 3)
+    W = shape.W
+
+    def ref(r, h):
+        sl = slice(r * W, (r + 1) * W)
+        f = lambda key: bf16_bits_to_f32(ep[key][:, sl, h, :])
+        return full_state_episode(ep["S0"][r, h], f("q"), f("k"), f("v"), ep["alpha"][:, sl, h],
+                                  ep["beta"][:, sl, h], ep["parents"][:, r, :])
+
+    r0, h0 = pairs[0]
+    out = ref(r0, h0)
+    exact = {(r0, h0): (out["o"].copy(), out["delta"].copy())}
+    res = bench.cpu_baseline(shape, ep, 3, gpu_outputs=exact)
+    assert res["max_abs_err_vs_gpu"]["o"] == 0.0 and res["max_abs_err_vs_gpu"]["delta"] == 0.0
+    assert res["max_abs_err_vs_gpu"]["pairs"] == 1              # distinct pairs checked
+    moved = (out["o"].copy(), out["delta"].copy())
+    moved[1][2, 5, 7] += 3e-4
+    res = bench.cpu_baseline(shape, ep, 3, gpu_outputs={(r0, h0): moved})
+    assert res["max_abs_err_vs_gpu"]["o"] == 0.0
+    assert abs(res["max_abs_err_vs_gpu"]["delta"] - 3e-4) < 1e-12
+    assert bench.cpu_baseline(shape, ep, 3)["max_abs_err_vs_gpu"] is None
