@@ -96,8 +96,9 @@ typedef struct onela_ctx onela_ctx;
  * (NULL = the null stream). Allocates S0 planes (4*H*d_v*d_k bytes per
  * request), the record store ((4 + 4*d_v + 2*d_k) bytes per record,
  * max_requests*H*max_steps*W records), the ancestry index
- * (2*max_requests*W*max_steps int32) and the per-request beam processing
- * order (2*max_requests*W int32). On failure *out is NULL. */
+ * (2*max_requests*W*max_steps int32), the per-request beam processing
+ * order (2*max_requests*W int32) and, for W <= 1024, the processing order of
+ * every step (max_requests*max_steps*W int32). On failure *out is NULL. */
 onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx** out);
 
 /* A context for another GDN layer of the same requests that reads the
@@ -107,15 +108,17 @@ onela_status onela_create(const onela_config* cfg, void* hip_stream, onela_ctx**
  * update per decode step serves every layer. cfg may differ from the owner's
  * in num_heads, d_k, d_v; max_requests, beam_width and max_steps must match
  * (else ONELA_E_INVALID_ARG; an owner cannot itself share another's index).
- * The owner's onela_step writes the index; a sharing context's step t of a
- * request reads the rows the owner's step t-1 wrote, so for every request:
- *   - the sharing context's step t (t >= 2) runs after the owner's step t-1
+ * The owner's onela_step writes the index and the order in which step t
+ * processes the beams (records are stored in that order, the same in every
+ * layer); a sharing context's step t of a request reads the rows the owner's
+ * step t-1 wrote and the order of the owner's step t, so for every request:
+ *   - the sharing context's step t (t >= 2) runs after the owner's step t
  *     and before the owner's step t+1 (else ONELA_E_BAD_STATE, nothing
  *     enqueued); when they use different streams the caller orders them;
  *   - after onela_init_request / onela_reset of a request on the owner, every
  *     sharing context that had stepped it must restart it too before its next
  *     step there (else ONELA_E_BAD_STATE).
- * Allocates what onela_create does minus the ancestry index and order.
+ * Allocates what onela_create does minus the ancestry index and orders.
  * Destroy sharing contexts before their owner (onela_destroy of an owner that
  * still has sharers returns ONELA_E_BAD_STATE and frees nothing). */
 onela_status onela_create_sharing_index(const onela_config* cfg, void* hip_stream, onela_ctx* index_owner,
@@ -282,13 +285,15 @@ onela_status onela_get_step(onela_ctx* ctx, int32_t req, int32_t* t_done);
 /* Ancestry rows the last step of `req` used (OneLA abstract: the ancestry
  * index lists the records that make up each beam's history): host int32
  * [W][max_steps]; row b holds t_done-1 record ids (oldest first) and -1
- * after them. */
+ * after them. Record id (j-1)*W + c names the record beam c appended at step
+ * j, whatever order the kernels stored the records in. */
 onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out);
 
 /* Records 0..n_rec-1 of (req, head), n_rec <= t_done*W (OneLA review,
- * evolve.pub, "Summary": a record holds (alpha_t, delta_t, k_t)). Host
- * outputs, each may be NULL: alpha float32 [n_rec], delta float32
- * [n_rec][d_v], key bf16 bits [n_rec][d_k]. */
+ * evolve.pub, "Summary": a record holds (alpha_t, delta_t, k_t)), record
+ * (j-1)*W + c being the one beam c appended at step j. Host outputs, each may
+ * be NULL: alpha float32 [n_rec], delta float32 [n_rec][d_v], key bf16 bits
+ * [n_rec][d_k]. */
 onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_t n_rec,
                                float* alpha, float* delta, uint16_t* key);
 

@@ -22,6 +22,7 @@ struct onela_ctx {
     uint16_t* rec_k = nullptr;
     int32_t* anc = nullptr;
     int32_t* order = nullptr;
+    int32_t* order_hist = nullptr;   // null when W > kOrderMax: records then sit at their beam index
     int32_t* err = nullptr;
     std::vector<int32_t> steps;      // steps done per request; -1 = never initialised
     std::vector<char> poisoned;      // a bad parent index was reported
@@ -171,7 +172,9 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
     const uint64_t nrec = R * H * T * W;
     ctx->s0_bytes = R * H * 2 * dv * dk * 2;
     ctx->rec_bytes = nrec * (4 + 4 * dv + 2 * dk);
-    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4) + 5 * R * 4;   // + error words, counters
+    const bool track = W <= (uint64_t)onela::kOrderMax;
+    ctx->idx_bytes = (owner ? 0 : 2 * R * W * T * 4 + 2 * R * W * 4 + (track ? R * T * W * 4 : 0)) +
+                     5 * R * 4;   // + error words, counters
 
     bool ok = hipMalloc(&ctx->s0_planes, ctx->s0_bytes) == hipSuccess &&
               hipMalloc(&ctx->rec_alpha, nrec * 4) == hipSuccess &&
@@ -181,7 +184,8 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
               hipMalloc(&ctx->dev_epoch, R * 4) == hipSuccess && hipMalloc(&ctx->err_cap, R * 4) == hipSuccess &&
               hipMalloc(&ctx->done, R * 4) == hipSuccess;
     if (ok && !owner)
-        ok = hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess && hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess;
+        ok = hipMalloc(&ctx->anc, 2 * R * W * T * 4) == hipSuccess && hipMalloc(&ctx->order, 2 * R * W * 4) == hipSuccess &&
+             (!track || hipMalloc(&ctx->order_hist, R * T * W * 4) == hipSuccess);
     if (!ok) {
         (void)hipGetLastError();
         onela_destroy(ctx);
@@ -200,6 +204,7 @@ static onela_status create_ctx(const onela_config* cfg, void* hip_stream, onela_
     if (owner) {
         ctx->anc = owner->anc;
         ctx->order = owner->order;
+        ctx->order_hist = owner->order_hist;
         ctx->index_owner = owner;
         owner->sharers.push_back(ctx);
     }
@@ -242,6 +247,7 @@ onela_status onela_destroy(onela_ctx* ctx) {
     } else {
         (void)hipFree(ctx->anc);
         (void)hipFree(ctx->order);
+        (void)hipFree(ctx->order_hist);
     }
     (void)hipFree(ctx->err);
     (void)hipFree(ctx->dev_steps);
@@ -368,9 +374,9 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
         if (ctx->steps[r] >= 1) need_parents = true;
         const int t = ctx->steps[r] + 1;
         // shared index: step t reads the rows the owner's step t-1 wrote, which
-        // the owner's step t+1 overwrites
-        if (ctx->index_owner && t >= 2 && ctx->index_owner->steps[r] != t - 1 && ctx->index_owner->steps[r] != t)
-            return ONELA_E_BAD_STATE;
+        // the owner's step t+1 overwrites, and the beam order of the owner's
+        // step t (where its records go)
+        if (ctx->index_owner && t >= 2 && ctx->index_owner->steps[r] != t) return ONELA_E_BAD_STATE;
         for (const onela_ctx* sh : ctx->sharers)
             if (t >= 2 && sh->steps[r] >= 1 && !sh->stale[r] && sh->steps[r] < t - 1) return ONELA_E_BAD_STATE;
     }
@@ -383,6 +389,7 @@ static onela_status step_impl(onela_ctx* ctx, int32_t n_req, const int32_t* reqs
     p.rec_k = ctx->rec_k;
     p.anc = ctx->anc;
     p.order = ctx->order;
+    p.order_hist = ctx->order_hist;
     p.err = ctx->err;
     p.write_index = ctx->index_owner ? 0 : 1;
     p.dev_steps = ctx->graph_mode ? ctx->dev_steps : nullptr;
@@ -472,6 +479,24 @@ onela_status onela_get_step(onela_ctx* ctx, int32_t req, int32_t* t_done) {
     return ctx->poisoned[req] ? ONELA_E_PARENT_RANGE : ONELA_OK;
 }
 
+// The beam at each processing position of the request's steps 1..n:
+// ord[j*W + i] = beam written at record j*W + i (the identity when the
+// kernels keep beam-index order, W > kOrderMax).
+static hipError_t load_order(onela_ctx* ctx, int32_t req, int n, std::vector<int32_t>& ord) {
+    const auto& c = ctx->cfg;
+    const size_t W = c.beam_width;
+    ord.resize((size_t)n * W);
+    if (!ctx->order_hist) {
+        for (size_t i = 0; i < ord.size(); ++i) ord[i] = (int32_t)(i % W);
+        return hipSuccess;
+    }
+    if (n == 0) return hipSuccess;
+    hipError_t e = hipMemcpy(ord.data(), ctx->order_hist + (size_t)req * c.max_steps * W, ord.size() * 4,
+                             hipMemcpyDeviceToHost);
+    for (int32_t& b : ord) b = (b < 0 || b >= (int32_t)W) ? 0 : b;   // (a valid order is a permutation)
+    return e;
+}
+
 onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out) {
     if (!ctx || !host_out || !valid_req(ctx, req)) return ONELA_E_INVALID_ARG;
     if (ctx->steps[req] < 0) return ONELA_E_BAD_STATE;
@@ -483,12 +508,19 @@ onela_status onela_get_ancestry(onela_ctx* ctx, int32_t req, int32_t* host_out) 
     const int t = ctx->steps[req];
     std::fill(host_out, host_out + n, -1);
     if (t >= 2) {
-        std::vector<int32_t> buf(n);
+        std::vector<int32_t> buf(n), ord;
         const int32_t* src = ctx->anc + ((size_t)(t & 1) * c.max_requests + req) * n;
         hipError_t e = hipMemcpy(buf.data(), src, n * 4, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = load_order(ctx, req, t - 1, ord);
         if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(anc)");
+        // stored ids name processing positions; reported ids name beams
+        const int64_t W = c.beam_width;
         for (int b = 0; b < c.beam_width; ++b)
-            for (int j = 0; j < t - 1; ++j) host_out[(size_t)b * c.max_steps + j] = buf[(size_t)b * c.max_steps + j];
+            for (int j = 0; j < t - 1; ++j) {
+                const int32_t r = buf[(size_t)b * c.max_steps + j];
+                host_out[(size_t)b * c.max_steps + j] =
+                    (r >= 0 && r < (t - 1) * W) ? (int32_t)((r / W) * W + ord[r]) : r;
+            }
     }
     return ONELA_OK;
 }
@@ -503,13 +535,34 @@ onela_status onela_get_records(onela_ctx* ctx, int32_t req, int32_t head, int32_
     if (s != ONELA_OK) return s;
     if ((int64_t)n_rec > (int64_t)ctx->steps[req] * c.beam_width) return ONELA_E_INVALID_ARG;
     if (ctx->poisoned[req]) return ONELA_E_PARENT_RANGE;
-    const size_t rec0 = ((size_t)req * c.num_heads + head) * (size_t)c.max_steps * c.beam_width;
-    hipError_t e = hipSuccess;
-    if (alpha && n_rec) e = hipMemcpy(alpha, ctx->rec_alpha + rec0, (size_t)n_rec * 4, hipMemcpyDeviceToHost);
-    if (e == hipSuccess && delta && n_rec)
-        e = hipMemcpy(delta, ctx->rec_delta + rec0 * c.d_v, (size_t)n_rec * 4 * c.d_v, hipMemcpyDeviceToHost);
-    if (e == hipSuccess && key && n_rec)
-        e = hipMemcpy(key, ctx->rec_k + rec0 * c.d_k, (size_t)n_rec * 2 * c.d_k, hipMemcpyDeviceToHost);
+    if (n_rec == 0) return ONELA_OK;
+    // Stored record j*W + i belongs to the beam at position i of step j+1;
+    // reported record (t-1)*W + b is beam b's.
+    const size_t W = c.beam_width, NREC = (size_t)c.max_steps * W;
+    const int n_steps = (int)((n_rec + W - 1) / W);
+    const size_t n_st = (size_t)n_steps * W;      // stored records covering the reported ones
+    std::vector<int32_t> ord;
+    hipError_t e = load_order(ctx, req, n_steps, ord);
+    std::vector<size_t> at(n_st);                 // stored index of reported record o
+    for (size_t r = 0; r < n_st; ++r) at[(r / W) * W + ord[r]] = r;
+    const size_t rec0 = ((size_t)req * c.num_heads + head) * NREC;
+    if (e == hipSuccess && alpha) {
+        std::vector<float> a(n_st);
+        e = hipMemcpy(a.data(), ctx->rec_alpha + rec0, n_st * 4, hipMemcpyDeviceToHost);
+        for (int o = 0; o < n_rec; ++o) alpha[o] = a[at[o]];
+    }
+    if (e == hipSuccess && delta) {
+        std::vector<float> d(n_st * c.d_v);
+        e = hipMemcpy(d.data(), ctx->rec_delta + rec0 * c.d_v, n_st * 4 * c.d_v, hipMemcpyDeviceToHost);
+        for (int o = 0; o < n_rec; ++o)
+            std::copy(&d[at[o] * c.d_v], &d[at[o] * c.d_v] + c.d_v, delta + (size_t)o * c.d_v);
+    }
+    if (e == hipSuccess && key) {
+        std::vector<uint16_t> kb(n_st * c.d_k);
+        e = hipMemcpy(kb.data(), ctx->rec_k + rec0 * c.d_k, n_st * 2 * c.d_k, hipMemcpyDeviceToHost);
+        for (int o = 0; o < n_rec; ++o)
+            std::copy(&kb[at[o] * c.d_k], &kb[at[o] * c.d_k] + c.d_k, key + (size_t)o * c.d_k);
+    }
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy(records)");
     return ONELA_OK;
 }

@@ -35,11 +35,15 @@ struct StepParams {
     float* delta_out;        // optional, like o
     // library state
     const uint16_t* s0_planes;  // [max_requests][H][2][DV*DK] in MFMA fragment order
+    // Records: record j*W + i is the one of step j+1 written by the beam at
+    // position i of that step's processing order (the beam index itself when
+    // W > kOrderMax).
     float* rec_alpha;           // [max_requests][H][T_max*W]
     float* rec_delta;           // [max_requests][H][T_max*W][DV]
     uint16_t* rec_k;            // [max_requests][H][T_max*W][DK]
-    int32_t* anc;               // [2][max_requests][W][T_max] (ping-pong by step parity)
-    int32_t* order;             // [2][max_requests][W] beam processing order (ping-pong by step parity)
+    int32_t* anc;               // [2][max_requests][W][T_max] record ids (ping-pong by step parity)
+    int32_t* order;             // [2][max_requests][W] beam at each position (ping-pong by step parity)
+    int32_t* order_hist;        // [max_requests][T_max][W] the same for every step (W <= kOrderMax)
     int32_t* err;               // [max_requests]: epoch of the last step that saw a bad parent
     // Graph mode (non-null dev_steps): each request's step and episode number
     // come from device memory, so a captured launch stays valid on replay.

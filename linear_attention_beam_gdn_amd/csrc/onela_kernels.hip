@@ -17,14 +17,15 @@
 //      P = S0 [k_t q_t], on the matrix cores (split-bf16: S0 = hi + lo);
 //   D. completes the replay in the MFMA accumulator registers, forms
 //      delta_t = beta (v - alpha y_k) and o_t = alpha y_q + (k_t . q_t) delta_t
-//      (= S_t q_t), and appends (alpha_t, delta_t, k_t).
+//      (= S_t q_t), and appends (alpha_t, delta_t, k_t) at the beam's
+//      processing position, so a chunk's records are adjacent.
 //
 // Wave w of the workgroup owns rows [16w, 16w+16) of d_v: its slice of S0
 // stays in registers as MFMA A-fragments for the whole beam loop, and every
 // step after the projection is row-separable, so no wave needs another
-// wave's rows. After the beam loop the alpha records and (one head per
-// request, unless the index belongs to another layer's context) the next
-// step's ancestry rows are written in beam-index order.
+// wave's rows. After the beam loop
+// (one head per request, unless the index belongs to another layer's
+// context) the next step's ancestry rows are written in beam-index order.
 //
 // Variants: in graph mode each request's step index comes from device
 // memory and the last workgroup of the request advances it; the FUSED
@@ -160,10 +161,10 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     float* at_s = kq_s + CH;                                        // [CH]: alpha_t
     float* bt_s = at_s + CH;                                        // [CH]: beta_t
     const int Wp = (p.W + 3) & ~3;                                   // W rounded up to whole int4s
-    int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] processing order (W <= kOrderMax)
-    int* pos_s = reinterpret_cast<int*>(xs);                        // [Wp] before the beam loop: step t-1 positions
-    int* ck_s = pos_s + Wp;                                         // [Wp] before the beam loop: sort keys
-    static_assert(!HIST || (2 * CH * XS + CH * VS) * 2 >= 2 * kOrderMax * 4, "order scratch fits in the k/q/v staging area");
+    int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] beam at each position of this step's order
+    int* posp_s = ord_s + Wp;                                       // [Wp] position of each beam in step t-1's order
+    int* ck_s = reinterpret_cast<int*>(xs);                         // [Wp] before the beam loop: sort keys
+    static_assert(!HIST || (2 * CH * XS + CH * VS) * 2 >= kOrderMax * 4, "sort keys fit in the k/q/v staging area");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -249,14 +250,25 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     const float dtb = FUSED ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.dt_bias[h]))) : 0.f;
     float* dout = p.delta_out ? p.delta_out + in0 * DV : nullptr;
     const int* parin = depth > 0 ? p.parent + (size_t)ri * W : nullptr;
+    // Record r of step j is the one written by the beam at position r - jW of
+    // step j's processing order, so the beams of a chunk append adjacent
+    // records and a chunk's ancestors of one depth are nearly adjacent too.
     float* ralpha = p.rec_alpha + rec0;                            // record r: ralpha[r]
-    float* rdelta = p.rec_delta + rec0 * DV;                       // record r: rdelta + r*DV
+    float* rdw = p.rec_delta + rec0 * DV + __builtin_amdgcn_readfirstlane(wave) * kRowsPerWave;   // wave's rows of record r: rdw + r*DV
     uint16_t* rkey = p.rec_k + rec0 * DK;                          // record r: rkey + r*DK
     const int* anc_prev = p.anc + ((size_t)((t - 1) & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* anc_next = p.anc + ((size_t)(t & 1) * p.max_requests + slot) * (size_t)W * p.T_max;
     int* ord_next = p.order + ((size_t)(t & 1) * p.max_requests + slot) * W;
 
-    const bool ordered = p.order_beams && W <= kOrderMax;
+    // Up to kOrderMax beams, every step has an order (the identity when not
+    // sorted), kept in an LDS table: ord_s maps positions to beams, posp_s the
+    // previous step's beams to their positions. The index owner sorts (when
+    // the host asks for it) and writes the order; a layer sharing the index
+    // reads the owner's order of this step, so every layer puts a beam's
+    // record at the same position.
+    const bool track = W <= kOrderMax;
+    const bool sharer = !p.write_index;
+    const bool ordered = track && !sharer && p.order_beams && depth > 0;
     __builtin_amdgcn_sched_barrier(0);
 
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
@@ -274,15 +286,11 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     // beam's sort key is its parent's position in step t-1's order (ties by
     // beam index), so siblings are adjacent and beams sharing older ancestors
     // are near each other; a chunk then gathers mostly records that no other
-    // chunk needs. The order only decides which beams share a chunk; each
-    // beam's arithmetic is independent of it. Every workgroup of a request
-    // derives the same order (a deterministic rank), and one workgroup of the
-    // index owner writes it for the next step. Wider beam sets than
-    // kOrderMax, and launches the host leaves unordered, keep the natural
-    // order (and write it, so that a later ordered step reads a permutation).
-    if (!ordered && W <= kOrderMax && p.write_index && h == 0 && split == 0)
-        for (int i = tid; i < W; i += NT) ord_next[i] = i;
-    if (ordered) {
+    // chunk needs. Each beam's arithmetic is independent of the order. Every
+    // workgroup of the owner derives the same order (a deterministic rank),
+    // and one of them writes it, for the next step and for the sharing layers
+    // of this one. Wider beam sets than kOrderMax keep the natural order.
+    if (track) {
         if (depth == 0) {
             for (int i = tid; i < W; i += NT) ord_s[i] = i;
         } else {
@@ -290,42 +298,59 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
             for (int u = 0; u < OU; ++u) {
                 const int i = tid + u * NT;
                 const int po = (depth & 1) ? po1[u] : po0[u];                 // order of step t-1
-                if (i < W) pos_s[min((unsigned)po, (unsigned)(W - 1))] = i;   // position of each step t-1 beam
-            }
-            lds_barrier();
-#pragma unroll
-            for (int u = 0; u < OU; ++u) {
-                const int i = tid + u * NT;
-                const int pb = pa[u];
-                if (i < Wp)   // unique composite keys; the padding sorts last
-                    ck_s[i] = i < W ? pos_s[(pb < 0 || pb >= W) ? 0 : pb] * W + i : 0x7fffffff;
-            }
-            lds_barrier();
-            // rank of each key among all keys: G adjacent lanes share a beam
-            // and split its key range, reading four keys per LDS access
-            int G = 1;
-            while (G < 8 && 2 * G * W <= NT) G <<= 1;
-            const int g = tid & (G - 1);
-            const int nq = Wp >> 2;
-            const int4* ck4 = reinterpret_cast<const int4*>(ck_s);
-            for (int b0 = 0; b0 < W; b0 += NT / G) {
-                const int b = b0 + tid / G;
-                const int c = ck_s[min(b, W - 1)];
-                int r = 0;
-#pragma unroll 4
-                for (int qd = g; qd < nq; qd += G) {
-                    const int4 kv = ck4[qd];
-                    r += (kv.x < c) + (kv.y < c) + (kv.z < c) + (kv.w < c);
+                const int pc = (depth & 1) ? po0[u] : po1[u];                 // the owner's order of step t
+                if (i < W) {
+                    posp_s[min((unsigned)po, (unsigned)(W - 1))] = i;         // position of each step t-1 beam
+                    if (sharer) ord_s[i] = min((unsigned)pc, (unsigned)(W - 1));
+                    else if (!ordered) ord_s[i] = i;
                 }
-                for (int m = 1; m < G; m <<= 1) r += __shfl_xor(r, m, 64);
-                if (g == 0 && b < W) ord_s[r] = b;
+            }
+            lds_barrier();
+            if (ordered) {
+#pragma unroll
+                for (int u = 0; u < OU; ++u) {
+                    const int i = tid + u * NT;
+                    const int pb = pa[u];
+                    if (i < Wp)   // unique composite keys; the padding sorts last
+                        ck_s[i] = i < W ? (int)min((unsigned)posp_s[(pb < 0 || pb >= W) ? 0 : pb], (unsigned)(W - 1)) * W + i
+                                        : 0x7fffffff;
+                    if (i < W) ord_s[i] = i;   // (overwritten by the ranks below)
+                }
+                lds_barrier();
+                // rank of each key among all keys: G adjacent lanes share a beam
+                // and split its key range, reading four keys per LDS access
+                int G = 1;
+                while (G < 8 && 2 * G * W <= NT) G <<= 1;
+                const int g = tid & (G - 1);
+                const int nq = Wp >> 2;
+                const int4* ck4 = reinterpret_cast<const int4*>(ck_s);
+                for (int b0 = 0; b0 < W; b0 += NT / G) {
+                    const int b = b0 + tid / G;
+                    const int c = ck_s[min(b, W - 1)];
+                    int r = 0;
+#pragma unroll 4
+                    for (int qd = g; qd < nq; qd += G) {
+                        const int4 kv = ck4[qd];
+                        r += (kv.x < c) + (kv.y < c) + (kv.z < c) + (kv.w < c);
+                    }
+                    for (int m = 1; m < G; m <<= 1) r += __shfl_xor(r, m, 64);
+                    if (g == 0 && b < W) ord_s[r] = b;
+                }
             }
         }
         lds_barrier();
-        if (p.write_index && h == 0 && split == 0)
-            for (int i = tid; i < W; i += NT) ord_next[i] = ord_s[i];
+        if (!sharer && h == 0 && split == 0) {
+            int* ord_hist = p.order_hist + ((size_t)slot * p.T_max + (t - 1)) * W;
+            for (int i = tid; i < W; i += NT) {
+                ord_next[i] = ord_s[i];
+                ord_hist[i] = ord_s[i];
+            }
+        }
     }
-    auto beam_at = [&](int i) __attribute__((always_inline)) { return ordered ? ord_s[i] : i; };
+    auto beam_at = [&](int i) __attribute__((always_inline)) { return track ? ord_s[i] : i; };
+    auto posp = [&](int x) __attribute__((always_inline)) {
+        return track ? (int)min((unsigned)posp_s[x], (unsigned)(W - 1)) : x;
+    };
 
     // The replay is linear in the records, so instead of the sequential
     //   y <- alpha_j y + (k_j . x) delta_j      (j = oldest .. newest)
@@ -407,7 +432,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
 #pragma unroll
                 for (int u = 0; u < kAncBatch; ++u) anc_s[min(j0 + u, depth - 1) * CH + tid_l] = row[u];
             }
-            anc_s[(depth - 1) * CH + tid_l] = (depth - 1) * W + par;   // parent's own record of step t-1
+            anc_s[(depth - 1) * CH + tid_l] = (depth - 1) * W + posp(par);   // parent's own record of step t-1
         }
         if constexpr (FUSED) {
             // a row's SEG pieces sit in SEG adjacent lanes of one wave
@@ -446,8 +471,10 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
             }
         }
         if (beam_thread) {
-            at_s[tid_l] = FUSED ? gate_alpha(a_new, neg_A, dtb) : a_new;
+            const float at = FUSED ? gate_alpha(a_new, neg_A, dtb) : a_new;
+            at_s[tid_l] = at;
             bt_s[tid_l] = FUSED ? gate_beta(b_new) : b_new;
+            ralpha[depth * W + c0 + tid_l] = at;          // alpha_t record, at the beam's position
         }
         lds_barrier();
 
@@ -539,7 +566,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
                 for (int u = 0; u < DBD; ++u) {
                     const int j = depth - 1 - u;
                     const int r = (bl < nb && j >= 0) ? anc_s[j * CH + bl] : 0;
-                    if constexpr (HIST) dd[u2][u] = *reinterpret_cast<const float4*>(rdelta + r * DV + rbase);
+                    if constexpr (HIST) dd[u2][u] = *reinterpret_cast<const float4*>(rdw + r * DV + quad * 4);
                     else dd[u2][u] = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
             }
@@ -570,7 +597,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
                         for (int u = 0; u < DBD; ++u)
                             if (jt - u >= 0)
                                 dd[u2][u] = *reinterpret_cast<const float4*>(
-                                    rdelta + anc_s[(jt - u) * CH + bl] * DV + rbase);
+                                    rdw + anc_s[(jt - u) * CH + bl] * DV + quad * 4);
                     }
 #pragma unroll
                     for (int u = 0; u < DBD; ++u) {
@@ -609,7 +636,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
                         make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
                 else
                     *reinterpret_cast<float4*>(oout + b * HV + rbase) = o;
-                *reinterpret_cast<float4*>(rdelta + (depth * W + b) * DV + rbase) = d;
+                *reinterpret_cast<float4*>(rdw + (depth * W + c0 + bl) * DV + quad * 4) = d;
                 if (dout) *reinterpret_cast<float4*>(dout + b * HV + rbase) = d;
             }
         }
@@ -620,18 +647,17 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
             const int idx = tid_l + it * NT;
             const int row = idx / SEG, seg = idx % SEG;
             if (idx < 2 * CH * SEG && row < nb)
-                *reinterpret_cast<uint4*>(rkey + (depth * W + beam_at(c0 + row)) * DK + seg * 8) =
+                *reinterpret_cast<uint4*>(rkey + (depth * W + c0 + row) * DK + seg * 8) =
                     *reinterpret_cast<const uint4*>(xs + row * XS + seg * 8);
         }
         lds_barrier();   // LDS is reused by the next chunk
     }
 
-    // ---- alpha_t records and the request's new index rows, in beam-index
-    // order over this workgroup's index range (the splits of a (request,
-    // head) cover [0, W) between them), so the small writes coalesce.
-    for (int b = b_begin + tid; b < b_end; b += NT) {
-        ralpha[depth * W + b] = FUSED ? gate_alpha(ain[b * H], neg_A, dtb) : ain[b * H];
-        if (p.write_index && h == 0 && depth > 0) {   // one head of the index owner writes it
+    // ---- the request's new index rows, in beam-index order over this
+    // workgroup's index range (the splits of a (request, head) cover [0, W)
+    // between them), so the small writes coalesce.
+    if (p.write_index && h == 0 && depth > 0) {   // one head of the index owner writes it
+        for (int b = b_begin + tid; b < b_end; b += NT) {
             int pb = parin[b];
             pb = (pb < 0 || pb >= W) ? 0 : pb;         // (reported in phase A)
             for (int j0 = 0; j0 + 1 < depth; j0 += kAncBatch) {   // (as the phase-A copy)
@@ -641,7 +667,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
 #pragma unroll
                 for (int u = 0; u < kAncBatch; ++u) anc_next[b * p.T_max + min(j0 + u, depth - 1)] = row[u];
             }
-            anc_next[b * p.T_max + depth - 1] = (depth - 1) * W + pb;
+            anc_next[b * p.T_max + depth - 1] = (depth - 1) * W + posp(pb);
         }
     }
     count_done();
@@ -739,7 +765,7 @@ size_t step_lds_bytes(int dk, int dv, int T_max, int W) {
            + kChunk * (size_t)(dv + 16) * 2       // vs
            + kChunk * ms * 4                      // anc_s
            + 3 * kChunk * 4                       // kq_s, at_s, bt_s
-           + (W <= kOrderMax ? (size_t)((W + 3) & ~3) * 4 : 0);   // ord_s
+           + (W <= kOrderMax ? 2 * (size_t)((W + 3) & ~3) * 4 : 0);   // ord_s, posp_s
 }
 
 bool step_supported(int dk, int dv) {

@@ -225,8 +225,11 @@ int main() {
         CHECK(onela_reset(ctx, 0) == ONELA_OK);
         CHECK(onela_step(ctx, 1, one, in.q, in.k, in.v, in.alpha, in.beta, nullptr, in.o, nullptr) == ONELA_OK);
         CHECK(onela_step(sharer, 1, one, in.q, in.k, in.v, in.alpha, in.beta, nullptr, in.o, nullptr) == ONELA_OK);
-        // the sharer's step 2 reads the rows of the owner's step 1; its step 3
-        // would read rows the owner has not written yet
+        // the sharer's step 2 reads the rows of the owner's step 1 and the beam
+        // order of the owner's step 2; its step 3 would need the owner's step 3
+        CHECK(onela_step(sharer, 1, one, in.q, in.k, in.v, in.alpha, in.beta, in.parents, in.o, nullptr) ==
+              ONELA_E_BAD_STATE);
+        CHECK(onela_step(ctx, 1, one, in.q, in.k, in.v, in.alpha, in.beta, in.parents, in.o, nullptr) == ONELA_OK);
         CHECK(onela_step(sharer, 1, one, in.q, in.k, in.v, in.alpha, in.beta, in.parents, in.o, nullptr) == ONELA_OK);
         CHECK(onela_step(sharer, 1, one, in.q, in.k, in.v, in.alpha, in.beta, in.parents, in.o, nullptr) ==
               ONELA_E_BAD_STATE);
@@ -237,7 +240,7 @@ int main() {
         CHECK(onela_step(sharer, 1, one, in.q, in.k, in.v, in.alpha, in.beta, in.parents, in.o, nullptr) ==
               ONELA_OK);
         CHECK(onela_sync(ctx) == ONELA_OK && onela_sync(sharer) == ONELA_OK);
-        CHECK(onela_get_step(ctx, 0, &t_done) == ONELA_OK && t_done == 2);
+        CHECK(onela_get_step(ctx, 0, &t_done) == ONELA_OK && t_done == 3);
         CHECK(onela_get_step(sharer, 0, &t_done) == ONELA_OK && t_done == 3);
         CHECK(onela_set_graph_mode(sharer, 0) == ONELA_OK);
         CHECK(onela_set_graph_mode(ctx, 0) == ONELA_OK);

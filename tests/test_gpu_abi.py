@@ -162,5 +162,10 @@ def test_memory_accounting():
     m = lay.memory()
     assert m["s0_bytes"] == shape.H * 128 * 128 * 4
     assert m["record_bytes"] == shape.H * shape.T * shape.W * (4 + 4 * 128 + 2 * 128)
-    assert m["index_bytes"] == 2 * shape.W * shape.T * 4 + 2 * shape.W * 4 + 5 * 4   # + 5 words per request
+    # ancestry rows (two parities), the order (two parities) and the order of
+    # every step, + 5 words per request
+    assert m["index_bytes"] == 2 * shape.W * shape.T * 4 + 2 * shape.W * 4 + shape.T * shape.W * 4 + 5 * 4
     lay.close()
+    wide = Onela(1, 1, 32, 32, 2048, 2)                 # wider than the ordered beam sets: no order history
+    assert wide.memory()["index_bytes"] == 2 * 2048 * 2 * 4 + 2 * 2048 * 4 + 5 * 4
+    wide.close()

@@ -148,9 +148,12 @@ def test_shared_index_ordering_rules():
 
     step(sharer, ep1, o1, 0)            # step 1 reads no index: any order
     with pytest.raises(OnelaError) as e:
-        step(sharer, ep1, o1, 1)        # step 2 before the owner's step 1
+        step(sharer, ep1, o1, 1)        # step 2 before the owner's steps 1 and 2
     assert e.value.status == -2
     step(owner, ep0, o0, 0)
+    with pytest.raises(OnelaError) as e:
+        step(sharer, ep1, o1, 1)        # the owner's step 2 decides where the records of step 2 go
+    assert e.value.status == -2
     step(owner, ep0, o0, 1)             # owner at 2, sharer at 1: fine
     with pytest.raises(OnelaError) as e:
         step(owner, ep0, o0, 2)         # owner's step 3 would overwrite what the sharer's step 2 reads
