@@ -48,11 +48,16 @@ def _close(layers):
         lay.close()
 
 
-def test_shared_index_layers_equal_independent_layers():
+@pytest.mark.parametrize("beam_order", [-1, 1])
+def test_shared_index_layers_equal_independent_layers(beam_order):
+    # beam_order 1: the owner processes the beams in ancestry order, so every
+    # step's records sit at permuted positions that the sharing layers must
+    # take from the owner's order
     eps = _layer_episodes()
-    print("[layers] 3 layers sharing one index vs independent", flush=True)
+    print(f"[layers] 3 layers sharing one index vs independent, beam order {beam_order}", flush=True)
     n = len(eps[0][1]["reqs"])
     layers = _make_layers(eps, n)
+    layers[0].set_beam_order(beam_order)
     for lay, (shape, ep, S0) in zip(layers, eps):
         for i in range(n):
             lay.init_request(i, gh.to_dev(S0[i]))
@@ -81,6 +86,10 @@ def test_shared_index_layers_equal_independent_layers():
             assert np.array_equal(o_np[t], ref["o"][t]), (li, t)
         for i in range(n):
             assert np.array_equal(lay.get_ancestry(i), ref["anc"][-1][i])
+            for h in range(shape.H):    # records by beam, whatever order they were stored in
+                got, want = lay.get_records(i, h, T * W), ref["layer"].get_records(i, h, T * W)
+                for g, w in zip(got, want):
+                    assert np.array_equal(g, w), (li, i, h)
         ref["layer"].close()
     mem = [lay.memory() for lay in layers]
     assert mem[1]["index_bytes"] == 20 * n and mem[2]["index_bytes"] == 20 * n   # per-request words only
