@@ -48,22 +48,24 @@ def _close(layers):
         lay.close()
 
 
-@pytest.mark.parametrize("beam_order", [-1, 1])
+@pytest.mark.parametrize("beam_order", [-1, 1, "alternating"])
 def test_shared_index_layers_equal_independent_layers(beam_order):
     # beam_order 1: the owner processes the beams in ancestry order, so every
     # step's records sit at permuted positions that the sharing layers must
-    # take from the owner's order
+    # take from the owner's order; "alternating": ancestry order at odd steps
+    # only, so orders and identity positions mix within one history
     eps = _layer_episodes()
     print(f"[layers] 3 layers sharing one index vs independent, beam order {beam_order}", flush=True)
     n = len(eps[0][1]["reqs"])
     layers = _make_layers(eps, n)
-    layers[0].set_beam_order(beam_order)
+    orders = [t % 2 for t in range(eps[0][0].T)] if beam_order == "alternating" else [beam_order] * eps[0][0].T
     for lay, (shape, ep, S0) in zip(layers, eps):
         for i in range(n):
             lay.init_request(i, gh.to_dev(S0[i]))
     outs = [[] for _ in layers]
     deltas = [[] for _ in layers]
     for t in range(eps[0][0].T):
+        layers[0].set_beam_order(orders[t])
         for li, (lay, (shape, ep, S0)) in enumerate(zip(layers, eps)):
             par = gh.to_dev(ep["parents"][t].astype(np.int32)) if t else None
             o = torch.full((n * shape.W, shape.H, shape.dv), float("nan"), dtype=torch.float32, device=gh.dev())
