@@ -23,7 +23,9 @@
  * Conventions used by this library (the pages do not fix them):
  *   - steps are t = 1..max_steps per episode; at t = 1 all beams start from
  *     S0 and parent_idx is ignored;
- *   - the record of beam b written at step t has id rid = (t-1)*W + b;
+ *   - the record of beam b written at step t has id rid = (t-1)*W + b (the
+ *     ids the inspection calls report; internally records are stored in the
+ *     order the kernels process the beams, and the index holds those ids);
  *   - ancestry row of beam b at step t = record ids of its t-1 ancestors,
  *     oldest first;
  *   - no query scaling and no normalisation inside: the caller folds those
