@@ -2,7 +2,7 @@
 import numpy as np
 import torch
 
-from workload import CONFIGS, bf16_bits_to_f32, decode_inputs, f32_to_bf16_bits, make_episode, shape_of
+from workload import WORKLOADS, bf16_bits_to_f32, decode_inputs, f32_to_bf16_bits, make_episode, shape_of
 from workload.gen import parents_for, prompt_tokens
 
 
@@ -42,8 +42,8 @@ def test_requests_independent_of_batch():
 
 
 def test_parent_rules_in_range():
-    for cfg in range(len(CONFIGS)):
-        s = CONFIGS[cfg]
+    for cfg in range(len(WORKLOADS)):
+        s = WORKLOADS[cfg]
         p = parents_for(s, 0)
         assert p.shape == (s.T, s.W)
         assert np.all(p[0] == -1)

@@ -5,7 +5,7 @@ random draws, the bf16 encoding of inputs and the parent-selection rules of the
 synthetic beam search, and none of the decode step's arithmetic.
 """
 from .gen import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Shape,
     bf16_bits_to_f32,
     decode_inputs,

@@ -49,7 +49,7 @@ class Shape:
     zipf_s: float = 1.2
 
 
-CONFIGS = (
+WORKLOADS = (
     Shape(0, "tiny_r1_h1_d32_w8_t3", 1, 1, 32, 32, 8, 3, "normal", 0.1, 0, "uniform"),
     Shape(1, "r1_h16_d128_w256_t3", 1, 16, 128, 128, 256, 3, "normal", 0.05, 0, "topw4"),
     Shape(2, "r1_h16_d128_w256_t7_prompt1024", 1, 16, 128, 128, 256, 7, "prompt", 0.0, 1024, "topw4"),
@@ -60,7 +60,7 @@ CONFIGS = (
 
 def shape_of(cfg: int, **overrides) -> Shape:
     """The shape of workload `cfg`, optionally with fields replaced."""
-    s = CONFIGS[cfg]
+    s = WORKLOADS[cfg]
     return replace(s, **overrides) if overrides else s
 
 
