@@ -127,9 +127,12 @@ def test_capacity_reset_and_rerun_identical():
     lay.close()
 
 
-def test_parent_out_of_range_poisons_request():
+@pytest.mark.parametrize("order,bad", [(-1, "W"), (1, "W"), (1, -7)])
+def test_parent_out_of_range_poisons_request(order, bad):
+    # (order 1: the bad parent also enters the ancestry-order sort, which clamps it)
     shape, ep, S0 = _small()
     lay = Onela(2, shape.H, 32, 32, shape.W, shape.T)
+    lay.set_beam_order(order)
     for r in (0, 1):
         lay.init_request(r, gh.to_dev(S0[0]))
     W = shape.W
@@ -138,7 +141,7 @@ def test_parent_out_of_range_poisons_request():
     ins = lambda t: (cat("q", t), cat("k", t), cat("v", t), cat("alpha", t), cat("beta", t))
     lay.step([0, 1], *ins(0), None, o)
     par = np.stack([ep["parents"][1][0], ep["parents"][1][0]]).astype(np.int32)
-    par[1, 3] = W                                   # request 1: one parent out of range
+    par[1, 3] = W if bad == "W" else bad            # request 1: one parent out of range
     lay.step([0, 1], *ins(1), gh.to_dev(par), o)
     with pytest.raises(OnelaError) as e:
         lay.sync()
