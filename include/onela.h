@@ -271,7 +271,7 @@ onela_status onela_set_beams_per_block(onela_ctx* ctx, int32_t beams);
  * Automatic orders a launch when its (request, head) pairs hold at least 32768
  * beams in all (below that a launch is bound by each workgroup's dependent
  * loads, which the ordering lengthens) and each beam set is split over at most
- * two workgroups (each workgroup ranks the whole set to process its share).
+ * two workgroups (each workgroup orders the whole set to process its share).
  * Results do not depend on it (every beam's arithmetic is its own); only the
  * records each chunk shares do. Returns ONELA_E_INVALID_ARG for any other
  * value. */

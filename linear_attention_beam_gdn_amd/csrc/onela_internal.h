@@ -18,8 +18,9 @@ constexpr int kOrderMax = 1024;
 // keep the natural beam order: they are bound by the latency of each
 // workgroup's dependent loads, which the ordering lengthens by one round, not
 // by the record traffic it saves. So do launches that split a beam set over
-// more than kOrderMaxSplits workgroups: each workgroup ranks all W beams (W^2
-// comparisons) to process only its share of them.
+// more than kOrderMaxSplits workgroups: each workgroup orders all W beams (a
+// comparison rank up to 256 beams, a radix sort above) to process only its
+// share of them.
 constexpr long kOrderMinBeams = 32768;
 constexpr int kOrderMaxSplits = 2;
 

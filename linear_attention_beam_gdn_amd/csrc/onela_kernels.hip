@@ -163,7 +163,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     const int Wp = (p.W + 3) & ~3;                                   // W rounded up to whole int4s
     int* ord_s = reinterpret_cast<int*>(bt_s + CH);                 // [Wp] beam at each position of this step's order
     int* posp_s = ord_s + Wp;                                       // [Wp] position of each beam in step t-1's order
-    int* ck_s = reinterpret_cast<int*>(xs);                         // [Wp] before the beam loop: sort keys
+    int* ck_s = reinterpret_cast<int*>(xs);                         // before the beam loop: sort keys or sort scratch
     static_assert(!HIST || (2 * CH * XS + CH * VS) * 2 >= kOrderMax * 4, "sort keys fit in the k/q/v staging area");
 
     const int tid = threadIdx.x;
@@ -269,6 +269,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
     const bool track = W <= kOrderMax;
     const bool sharer = !p.write_index;
     const bool ordered = track && !sharer && p.order_beams && depth > 0;
+    constexpr int kRankMaxW = 256;   // widest beam set ranked by comparisons; wider ones are radix-sorted
     __builtin_amdgcn_sched_barrier(0);
 
     // This wave's rows of S0 as A-fragments, resident for the whole beam loop.
@@ -306,7 +307,7 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
                 }
             }
             lds_barrier();
-            if (ordered) {
+            if (ordered && W <= kRankMaxW) {
 #pragma unroll
                 for (int u = 0; u < OU; ++u) {
                     const int i = tid + u * NT;
@@ -336,6 +337,89 @@ __device__ __forceinline__ void step_body(const StepParams& p) {
                     for (int m = 1; m < G; m <<= 1) r += __shfl_xor(r, m, 64);
                     if (g == 0 && b < W) ord_s[r] = b;
                 }
+            } else if (ordered) {
+                // Stable LSD radix sort of the beams, from index order, by the
+                // parent's position in step t-1's order, RB bits a pass: the order
+                // of the keys (parent position, beam index). Each entry packs the
+                // parent position above the beam index. Per pass, every 64-beam
+                // chunk counts its digits and ranks its beams within the chunk by
+                // ballots; a scan of the counts (digit-major) gives every chunk's
+                // first slot per digit, and each beam moves to its slot.
+                static_assert(kOrderMax <= 1024, "beam index in 10 bits");
+                constexpr int SCR = (2 * CH * XS + CH * VS) * 2;              // bytes of the staging area
+                constexpr int NCHM = kOrderMax / 64;
+                constexpr int RB = 2 * kOrderMax * 4 + 32 * NCHM * 4 <= SCR ? 5 : 4;
+                constexpr int RD = 1 << RB;
+                static_assert(2 * kOrderMax * 4 + RD * NCHM * 4 <= SCR, "sort scratch fits in the staging area");
+                constexpr int CPW = (NCHM + NW - 1) / NW;                     // chunks per wave
+                const int nch = (W + 63) >> 6;
+                int* sqa = ck_s;                                              // [Wp] (parent position << 10) | beam
+                int* sqb = sqa + Wp;                                          // [Wp]
+                int* hs = sqb + Wp;                                           // [RD][nch] counts, then first slots
+#pragma unroll
+                for (int u = 0; u < OU; ++u) {
+                    const int i = tid + u * NT;
+                    const int pb = pa[u];
+                    if (i < W)
+                        sqa[i] = (int)(min((unsigned)posp_s[(pb < 0 || pb >= W) ? 0 : pb], (unsigned)(W - 1)) << 10) | i;
+                }
+                lds_barrier();
+                const int nbits = W > 1 ? 32 - __clz(W - 1) : 0;
+                for (int sh = 0; sh < nbits; sh += RB) {
+                    int ent[CPW], dg[CPW], rk[CPW];
+#pragma unroll
+                    for (int k = 0; k < CPW; ++k) {
+                        const int c = wave + k * NW;
+                        const int i = c * 64 + lane;
+                        const bool valid = c < nch && i < W;
+                        ent[k] = valid ? sqa[i] : 0;
+                        dg[k] = valid ? (ent[k] >> (10 + sh)) & (RD - 1) : RD;   // RD: no beam
+                        rk[k] = 0;
+                        if (c < nch) {                                        // (uniform in the wave)
+#pragma unroll 1
+                            for (int v = 0; v < RD; ++v) {
+                                const unsigned long long m = __ballot(dg[k] == v);
+                                if (dg[k] == v)
+                                    rk[k] = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+                                if (lane == v) hs[v * nch + c] = __popcll(m);
+                            }
+                        }
+                    }
+                    lds_barrier();
+                    if (wave == 0) {                                          // exclusive scan, digit-major
+                        constexpr int EM = (RD * NCHM + 63) / 64;
+                        const int S = RD * nch;
+                        int loc[EM], sum = 0;
+#pragma unroll
+                        for (int e = 0; e < EM; ++e) {
+                            const int j = lane * EM + e;
+                            loc[e] = j < S ? hs[j] : 0;
+                            sum += loc[e];
+                        }
+                        int x = sum;
+#pragma unroll
+                        for (int o = 1; o < 64; o <<= 1) {
+                            const int y = __shfl_up(x, o, 64);
+                            if (lane >= o) x += y;
+                        }
+                        int run = x - sum;
+#pragma unroll
+                        for (int e = 0; e < EM; ++e) {
+                            const int j = lane * EM + e;
+                            if (j < S) hs[j] = run;
+                            run += loc[e];
+                        }
+                    }
+                    lds_barrier();
+#pragma unroll
+                    for (int k = 0; k < CPW; ++k)
+                        if (dg[k] < RD) sqb[hs[dg[k] * nch + wave + k * NW] + rk[k]] = ent[k];
+                    lds_barrier();
+                    int* tmp = sqa;
+                    sqa = sqb;
+                    sqb = tmp;
+                }
+                for (int i = tid; i < W; i += NT) ord_s[i] = sqa[i] & 1023;
             }
         }
         lds_barrier();
