@@ -215,6 +215,19 @@ def test_more_requests_than_one_launch():
     outs["layer"].close()
 
 
+@pytest.mark.parametrize("W,d,parents,bpb", [(257, 32, "zipf", 0), (500, 64, "topw4", 0), (777, 32, "uniform", 128),
+                                            (1024, 128, "zipf", 0), (1024, 32, "topw4", 256)])
+def test_parity_wide_beam_sets_in_ancestry_order(W, d, parents, bpb):
+    """Ancestry order forced on beam sets wider than 256, which are radix-sorted:
+    ragged chunk counts, several chunks per wave, both digit widths."""
+    shape = shape_of(0, name=f"wide_w{W}_d{d}", R=2, H=2, dk=d, dv=d, W=W, T=5, parents=parents)
+    ep, S0 = gh.episode(shape)
+    print(f"[parity] wide W={W} d={d} parents={parents} beams_per_block={bpb} beam_order=1", flush=True)
+    outs = gh.run_episode(shape, ep, S0, beams_per_block=bpb, beam_order=1)
+    _check_pairs(shape, ep, S0, outs, [(i, h) for i in range(2) for h in range(2)])
+    outs["layer"].close()
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_parity_random_shapes(seed):
     """Seeded random shapes, parent patterns, gate extremes, launch shapes and
