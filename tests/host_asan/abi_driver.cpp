@@ -172,6 +172,7 @@ int main() {
     std::vector<uint16_t> rk(static_cast<size_t>(n_rec) * D);
     CHECK(onela_get_records(ctx, 1, H - 1, n_rec, ra.data(), rd.data(), rk.data()) == ONELA_OK);
     CHECK(onela_get_records(ctx, 1, H - 1, n_rec, nullptr, rd.data(), nullptr) == ONELA_OK);
+    CHECK(onela_get_records(ctx, 1, 0, n_rec - W + 3, ra.data(), rd.data(), rk.data()) == ONELA_OK);   // ends inside a step
     CHECK(onela_get_records(ctx, 1, H, n_rec, ra.data(), nullptr, nullptr) == ONELA_E_INVALID_ARG);
     CHECK(onela_get_records(ctx, 1, 0, n_rec + 1, ra.data(), nullptr, nullptr) == ONELA_E_INVALID_ARG);
     uint64_t s0b = 0, recb = 0, idxb = 0;
