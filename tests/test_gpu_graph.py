@@ -27,20 +27,23 @@ LAYERS = [(4, 128), (2, 64)]   # (heads, head dim); layer 0 owns the ancestry in
 KEYS = ("q", "k", "v", "alpha", "beta")
 
 
-def test_graph_replay_of_a_two_layer_decode_step():
+@pytest.mark.parametrize("W,order", [(256, -1), (600, 1)])
+def test_graph_replay_of_a_two_layer_decode_step(W, order):
+    # (600 beams in ancestry order: the captured launches sort them by the radix sort)
     eps = []
     for H, d in LAYERS:
-        shape = shape_of(1, name="graph", R=2, H=H, dk=d, dv=d, T=4)
+        shape = shape_of(1, name="graph", R=2, H=H, dk=d, dv=d, T=4, W=W)
         eps.append((shape,) + tuple(gh.episode(shape)))
     shape0 = eps[0][0]
     n, W, T = len(eps[0][1]["reqs"]), shape0.W, shape0.T
-    print("[graph] two layers, one captured decode step, replayed", flush=True)
+    print(f"[graph] two layers, one captured decode step, replayed; W={W} beam_order={order}", flush=True)
     refs = [gh.run_episode(shape, ep, S0) for shape, ep, S0 in eps]   # eager, independent contexts
 
     s = torch.cuda.Stream()
     owner = Onela(n, shape0.H, shape0.dk, shape0.dv, W, T, stream=s)
     sharer = Onela(n, eps[1][0].H, eps[1][0].dk, eps[1][0].dv, W, T, stream=s, share_index_of=owner)
     layers = [owner, sharer]
+    owner.set_beam_order(order)
     for lay, (shape, ep, S0) in zip(layers, eps):
         lay.set_graph_mode(True)
         for i in range(n):
